@@ -1,0 +1,239 @@
+"""Benchmark: paged decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|3|4a|4b|5d|5p] [--no-cpu-baseline]
+
+A step is one paged_attn_decode call (all G query heads of every KV head,
+every sequence of the batch, split-context merge included) over one layer's
+cache. The default workload is the Llama-3-8B-shaped bf16 decode layer (32
+query / 8 KV heads, d 128, 64 sequences with context U[512, 4096], seed
+4292). Inputs are seeded synthetic N(0,1) data written into device pools
+before timing; steps cycle through several identical copies of the layer's
+pools (as a model's layers would) so that consecutive steps do not re-read
+the same memory from the last-level cache.
+
+The line printed carries the achieved HBM bandwidth over algorithmic bytes
+(K/V of every attended token once per KV head, plus Q, O, the table entries
+and lengths read), the decode tokens/s per layer, a roofline object for the
+decode kernel (HIP-event time on the launch stream) and the CPU oracle's
+throughput on the host (a bounded sample of the same workload).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+# thread counts for the CPU oracle's BLAS, fixed before numpy loads
+try:
+    _CORES = len(os.sched_getaffinity(0))
+except AttributeError:  # pragma: no cover
+    _CORES = os.cpu_count() or 1
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_v, str(_CORES))
+
+import numpy as np  # noqa: E402
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: achieved HBM GB/s (% of peak) and decode tokens/s per layer"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="2")
+    ap.add_argument("--layers", type=int, default=4, help="copies of the layer's pools cycled through")
+    ap.add_argument("--partition-blocks", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def decode_bytes(case, kv_bits):
+    """Algorithmic bytes of one decode step: every attended token's K and V
+    once per KV head (shared blocks once), scales, Q, O, table entries, lengths."""
+    n_kv, d = case.n_kv, case.d
+    ctx = case.context_lens.astype(np.int64)
+    nblk = -(-ctx // 16)
+    if case.shared_prefix_blocks:
+        P = case.shared_prefix_blocks
+        tokens = P * 16 + int(np.sum(ctx - P * 16))
+        blocks = P + int(np.sum(nblk - P))
+    else:
+        tokens = int(ctx.sum())
+        blocks = int(nblk.sum())
+    elem = 2 if case.dtype == "bf16" else 4
+    kv = tokens * n_kv * d * 2 * kv_bits / 8
+    scales = blocks * n_kv * 2 * 2 if kv_bits < 16 else 0
+    qo = 2 * case.num_seqs * case.n_heads * d * elem
+    meta = int(nblk.sum()) * 4 + case.num_seqs * 4
+    return kv + scales + qo + meta
+
+
+def build_case(workload):
+    from synth import make_config_case, make_mixed_case
+    if workload in ("2", "3"):
+        return make_config_case(int(workload)), 16
+    if workload in ("4a", "4b"):
+        return make_config_case(4), 8 if workload == "4a" else 4
+    if workload == "5d":
+        return make_mixed_case()[1], 16
+    raise SystemExit(f"unknown workload {workload}")
+
+
+def to_dev(x, dtype, torch):
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def cpu_baseline(case, kv_bits, budget_s):
+    """The oracle, as it stands, on whole sequences of the same workload until
+    about `budget_s` seconds of host time; throughput in the metric's unit.
+    Decoding the pools to float64 (and quantizing them, for int KV) is
+    preparation and is not timed; gather + attention are."""
+    import oracle
+    q = oracle.as_f64(case.q, case.dtype)
+    if kv_bits < 16:
+        kc, ksc = oracle.quantize_tiles(oracle.as_f64(case.k_slots, case.dtype).astype(np.float32), kv_bits)
+        vc, vsc = oracle.quantize_tiles(oracle.as_f64(case.v_slots, case.dtype).astype(np.float32), kv_bits)
+        kf, vf = oracle.dequantize(kc, ksc), oracle.dequantize(vc, vsc)
+        del kc, vc
+    else:
+        kf, vf = oracle.as_f64(case.k_slots, case.dtype), oracle.as_f64(case.v_slots, case.dtype)
+    order = np.random.default_rng(0).permutation(case.num_seqs)
+    done = []
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 <= budget_s:  # whole sequences, repeating the batch if it is short
+        s = int(order[len(done) % len(order)])
+        oracle.paged_decode(q, kf, vf, case.block_tables, case.context_lens, n_kv=case.n_kv, seqs=[s])
+        done.append(s)
+    el = time.perf_counter() - t0
+    sub = case.context_lens[done].astype(np.int64)
+    per_tok = case.n_kv * case.d * 2 * kv_bits / 8
+    elem = 2 if case.dtype == "bf16" else 4
+    byts = float(sub.sum()) * per_tok + 2 * len(done) * case.n_heads * case.d * elem
+    return {
+        "value": round(byts / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": _CORES,
+        "kind": "oracle",
+        "sample": (f"{len(done)} sequence decodes drawn from the {case.num_seqs}-sequence batch "
+                   f"({int(sub.sum())} context tokens) in {el:.1f} s; float64 NumPy, all heads"),
+        "seqs_per_s": round(len(done) / el, 3),
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from paged_kv_cache_429_amd import binding as B
+    from synth import CONFIGS
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    t_gen = time.perf_counter()
+    case, kv_bits = build_case(a.workload)
+    gen_s = time.perf_counter() - t_gen
+
+    # device pools: one bf16 copy written by paged_kv_write, quantized if asked,
+    # then replicated for `layers` layers
+    src_bits = 32 if case.dtype == "f32" else 16
+    kp = B.alloc_pool(case.num_blocks, case.n_kv, case.d, src_bits)
+    vp = B.alloc_pool(case.num_blocks, case.n_kv, case.d, src_bits)
+    slots = torch.arange(case.num_blocks * 16, dtype=torch.int64, device="cuda")
+    B.kv_write(to_dev(case.k_slots, case.dtype, torch), to_dev(case.v_slots, case.dtype, torch), slots, kp, vp,
+               n_kv_heads=case.n_kv)
+    ks = vs = None
+    if kv_bits < 16:
+        kp, ks = B.quantize(kp, bits=kv_bits, kind=0, n_kv_heads=case.n_kv, d_head=case.d)
+        vp, vs = B.quantize(vp, bits=kv_bits, kind=1, n_kv_heads=case.n_kv, d_head=case.d)
+    layers = [(kp, vp, ks, vs)]
+    for _ in range(a.layers - 1):
+        layers.append(tuple(None if t is None else t.clone() for t in (kp, vp, ks, vs)))
+    q = to_dev(case.q, case.dtype, torch)
+    tables = torch.from_numpy(np.ascontiguousarray(case.block_tables)).cuda()
+    ctx = torch.from_numpy(np.ascontiguousarray(case.context_lens)).cuda()
+    out = torch.empty_like(q)
+    mcl = case.max_context_len
+    ws = B.decode_workspace(case.num_seqs, case.n_heads, case.n_kv, case.d, mcl, a.partition_blocks)
+    torch.cuda.synchronize()
+
+    def step(i):
+        k_, v_, ks_, vs_ = layers[i % len(layers)]
+        B.decode(q, k_, v_, tables, ctx, n_kv_heads=case.n_kv, max_context_len=mcl, kv_bits=kv_bits,
+                 k_scales=ks_, v_scales=vs_, out=out, workspace=ws, partition_blocks=a.partition_blocks)
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = np.array([s.elapsed_time(e) for s, e in ev])
+
+    byts = decode_bytes(case, kv_bits)
+    ms_step = wall * 1e3 / a.steps
+    value = byts / (ms_step * 1e-3) / 1e9
+    k_avg = float(kern_ms.mean())
+    achieved = byts / (k_avg * 1e-3) / 1e9
+    name = {"2": 2, "3": 3, "4a": 4, "4b": 4, "5d": 5}[a.workload]
+    wl = CONFIGS[name]["workload"] + ({"4a": " [int8]", "4b": " [int4]", "5d": " [decode half]"}.get(a.workload, ""))
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {32: "f32", 16: "bf16", 8: "bf16 q / int8 kv", 4: "bf16 q / int4 kv"}[kv_bits],
+        "data": "synthetic",
+        "config": {
+            "workload": wl,
+            "num_seqs": case.num_seqs, "n_heads": case.n_heads, "n_kv_heads": case.n_kv, "d_head": case.d,
+            "block_size": 16, "kv_bits": kv_bits, "total_context_tokens": int(case.context_lens.sum()),
+            "max_context_len": mcl, "seed": case.seed, "layers_cycled": a.layers,
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s_per_layer": round(case.num_seqs / (ms_step * 1e-3), 1),
+        "algorithmic_bytes_per_step": int(byts),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_kernel",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel_avg_us": round(k_avg * 1e3, 3),
+            "kernel_p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
+            "kernel_p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 3),
+        },
+        "input_generation_s": round(gen_s, 2),
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(case, kv_bits, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

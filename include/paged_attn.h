@@ -1,0 +1,219 @@
+/*
+ * paged_attn.h -- paged-KV-cache attention for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels:
+ *   paged_attn_decode         single-query attention of a batch of sequences
+ *   paged_attn_prefill_chunk  causal attention of a chunk of prompt tokens
+ *   kv_quantize               symmetric int8 / int4 codes + fp16 scales
+ *   paged_kv_write            scatter new tokens' K/V into their cache slots
+ * plus a few host-only helpers (sizes, error strings).
+ *
+ * Sources (three web pages on KV caching, cited by title and section):
+ *   [TAI] "KV cache, continuous batching and paged attention"
+ *   [IR]  "KV cache, GQA, paging and continuous batching"
+ *   [JE]  jovanaeducation inference guide a2-inf-2
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions shared by every entry point
+ * ---------------------------------------------------------------------------
+ * Memory. Every array argument is caller-owned device memory of the current
+ * HIP device, unless stated otherwise; the library never allocates, frees or
+ * retains a pointer after the call returns.
+ *
+ * Streams. `stream` is a hipStream_t passed as void* (NULL = the null
+ * stream). Every call only enqueues work on that stream and returns; results
+ * are ready once the stream reaches that point. The host never reads device
+ * data, so no call synchronises.
+ *
+ * Errors. Each call returns PA_OK or a negative pa_status. Argument errors
+ * are detected on the host before any device work is enqueued (nothing is
+ * written). PA_ERR_HIP means a HIP launch call failed; a fault inside a
+ * kernel surfaces as a HIP error at the caller's next synchronisation.
+ * The only mutable global state is a per-device cache of the compute-unit
+ * count (atomic); calls may be made from several host threads on different
+ * streams.
+ *
+ * Paging ([TAI] "Paged attention"; [IR] "PagedAttention: why fragmentation
+ * was eating most of the rest"). The cache of one layer is a pool of
+ * `num_blocks` physical blocks of `block_size` = 16 token slots each. A
+ * sequence's logical token t lives in slot t % 16 of physical block
+ * block_tables[s * max_blocks_per_seq + t / 16]. Physical blocks may be
+ * shared between sequences (common prefixes, [JE] "Prefix caching"); the
+ * kernels follow the table and never write the pool. Only the entries
+ * j < ceil(ctx_s / 16) of a row are read. Block ids outside [0, num_blocks)
+ * are a caller error: the kernels replace them by block 0 (never reading out
+ * of bounds), so results for that sequence are then meaningless.
+ *
+ * GQA ([IR] "What it is" and the table in "The memory equation"): query head
+ * h reads KV head h / G, G = n_heads / n_kv_heads (contiguous groups);
+ * n_kv_heads = n_heads is MHA, n_kv_heads = 1 is MQA. 1 <= G <= 16.
+ *
+ * Attention ([JE] the figure of attention as a soft query-key-value lookup;
+ * [IR] "What it is"): o = softmax(q K^T / sqrt(d_head)) V with float32
+ * accumulation. The pages lose the formula; the 1/sqrt(d_head) scale is the
+ * standard reading and is not an argument.
+ *
+ * ---------------------------------------------------------------------------
+ * Device layout of the K/V pools
+ * ---------------------------------------------------------------------------
+ * kv_bits gives the element format of the pools:
+ *   32  float32            (requires dtype == PA_F32)
+ *   16  bfloat16           (requires dtype == PA_BF16)
+ *    8  int8 code  + fp16 scale per (block, KV head) (requires PA_BF16)
+ *    4  int4 code  + fp16 scale per (block, KV head) (requires PA_BF16)
+ * A pool is an array of tiles, one per (block b, KV head h), each holding the
+ * 16 slots x d_head elements of that block and head, at byte offset
+ *     ((size_t)b * n_kv_heads + h) * tile_bytes,  tile_bytes = 16*d_head*kv_bits/8.
+ * Inside a tile, element (slot t, dim i) is element number
+ *     K pool:  ((i / x) * 16 + t) * x + i % x,   x = 128 / kv_bits
+ *              (16-byte chunks of x consecutive dims, slot-minor)
+ *     V pool:  i * 16 + t                          (transposed: dim-major)
+ * of the tile, elements packed at kv_bits each, little-endian; for int4 the
+ * even-numbered element of a pair is the low nibble. Codes are two's
+ * complement. Scales are float16 bit patterns, k_scales / v_scales
+ * [num_blocks][n_kv_heads]; value = code * scale.
+ * Supported d_head: 64 and 128.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = -1,  /* a pointer, size or shape is invalid            */
+    PA_ERR_UNSUPPORTED = -2,  /* valid, but not a shape/format this build runs  */
+    PA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required     */
+    PA_ERR_HIP = -4           /* a HIP runtime call failed                      */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+typedef enum pa_kv_kind { PA_KIND_K = 0, PA_KIND_V = 1 } pa_kv_kind;
+
+#define PA_BLOCK_SIZE 16
+#define PA_MAX_GROUP 16
+
+/* Human-readable text of a status code (static storage). */
+const char* pa_error_string(int status);
+
+/* Bytes of one (block, KV head) tile: 16 * d_head * kv_bits / 8; 0 if the
+ * arguments are invalid. Host only. */
+size_t pa_tile_bytes(int d_head, int kv_bits);
+
+/* KV bytes per token, all layers: 2 (K and V) x n_layers x n_kv_heads x
+ * d_head x kv_bits/8 ([TAI] "The KV cache"; [IR] "The memory equation").
+ * Host only. */
+uint64_t pa_kv_bytes_per_token(int n_layers, int n_kv_heads, int d_head, int kv_bits);
+
+/* Bytes a paged cache holds for one sequence of n_tokens: whole 16-token
+ * blocks of K and V in every layer, plus the two fp16 scales per (block, KV
+ * head) of a quantized cache. Host only. */
+uint64_t pa_kv_cache_bytes(int n_layers, int n_kv_heads, int d_head, int kv_bits, int64_t n_tokens);
+
+/* ---------------------------------------------------------------------------
+ * Decode ([TAI] "Paged attention": the attention kernel follows the block
+ * table; [TAI] "The KV cache": each step attends over the cached K/V of all
+ * earlier tokens).
+ *
+ * q            [num_seqs][n_heads][d_head] of dtype
+ * k_pool/v_pool  pools in the layout above (read only)
+ * k_scales/v_scales  fp16 [num_blocks][n_kv_heads]; NULL unless kv_bits < 16
+ * block_tables int32 [num_seqs][max_blocks_per_seq]
+ * context_lens int32 [num_seqs]: tokens to attend, including the token being
+ *              decoded (its K/V must already be in the pool). Values are
+ *              clamped to min(max_context_len, 16 * max_blocks_per_seq); a
+ *              value <= 0 yields a zero output row.
+ * max_context_len  host-side upper bound of context_lens (plans the split)
+ * out          [num_seqs][n_heads][d_head] of dtype (written)
+ * workspace    device scratch of at least paged_attn_decode_workspace_size()
+ *              bytes (may be NULL when that size is 0): the partials of
+ *              split sequences. Its contents on entry do not matter. Calls
+ *              that share a workspace must be ordered (same stream, or
+ *              synchronised); overlapping calls on one workspace race.
+ * partition_blocks  blocks per context partition (even, 2..64), or 0 to let
+ *              the library choose. Long contexts are split into partitions
+ *              processed in parallel and merged by log-sum-exp in a second
+ *              kernel on the same stream (launched only when some sequence
+ *              can span more than one partition); the split depends only on
+ *              the arguments' values on the host and on each sequence's
+ *              length, never on physical block ids.
+ * ------------------------------------------------------------------------ */
+size_t paged_attn_decode_workspace_size(int num_seqs, int n_heads, int n_kv_heads, int d_head,
+                                        int max_context_len, int partition_blocks);
+
+int paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
+                      const uint16_t* k_scales, const uint16_t* v_scales,
+                      const int32_t* block_tables, int max_blocks_per_seq,
+                      const int32_t* context_lens, int max_context_len,
+                      int num_seqs, int num_blocks, int block_size,
+                      int n_heads, int n_kv_heads, int d_head, int dtype, int kv_bits,
+                      void* out, void* workspace, size_t workspace_bytes,
+                      int partition_blocks, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Causal prefill of a chunk ([JE] "Chunked prefill"; [TAI] "Scheduling
+ * prefill and decode": a long prompt is split into chunks that run beside
+ * decodes; each chunk is the same attention over the cache, split up).
+ *
+ * Sequence s contributes q_len_s = cu_q_lens[s+1] - cu_q_lens[s] query rows,
+ * rows cu_q_lens[s] .. cu_q_lens[s+1]-1 of q. They are its last q_len_s
+ * tokens: row i sits at absolute position context_lens[s] - q_len_s + i and
+ * attends keys 0..that position (inclusive). The chunk's own K/V must already
+ * be in the pool.
+ * q, out        [total_q][n_heads][d_head] of dtype
+ * cu_q_lens     int32 [num_seqs + 1] device prefix sums, cu_q_lens[0] = 0,
+ *               cu_q_lens[num_seqs] = total_q, 0 <= q_len_s <= max_q_len,
+ *               q_len_s <= context_lens[s]
+ * other arguments as for paged_attn_decode. No workspace.
+ * ------------------------------------------------------------------------ */
+int paged_attn_prefill_chunk(const void* q, const int32_t* cu_q_lens, int total_q, int max_q_len,
+                             const void* k_pool, const void* v_pool,
+                             const uint16_t* k_scales, const uint16_t* v_scales,
+                             const int32_t* block_tables, int max_blocks_per_seq,
+                             const int32_t* context_lens, int max_context_len,
+                             int num_seqs, int num_blocks, int block_size,
+                             int n_heads, int n_kv_heads, int d_head, int dtype, int kv_bits,
+                             void* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Symmetric b-bit quantization of a bf16 pool ([JE] "KV-cache quantization":
+ * each key/value becomes an integer sharing one scale s with its group).
+ * Group = one (block, KV head) tile, 16 slots x d_head:
+ *   s    = float16_rne( float32(amax |x|) / qmax ),  qmax = 127 (8 bit), 7 (4 bit)
+ *   code = clamp( rint_half_even( x / float32(s) ), -qmax, qmax ), 0 if s == 0
+ * (float32 IEEE division). src must be finite; a scale that overflows fp16
+ * is stored as +inf with all codes 0.
+ * src     bf16 pool of `kind` (K or V layout, kv_bits = 16)
+ * codes   int pool of the same kind with kv_bits = bits (written)
+ * scales  fp16 [num_blocks][n_kv_heads] (written for the processed blocks)
+ * block_ids  int32 [n_ids] blocks to process, or NULL for all num_blocks
+ *            (ids outside [0, num_blocks) are skipped)
+ * ------------------------------------------------------------------------ */
+int kv_quantize(const void* src, void* codes, uint16_t* scales,
+                const int32_t* block_ids, int n_ids,
+                int num_blocks, int n_kv_heads, int block_size, int d_head,
+                int bits, int kind, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Write new tokens' keys/values into their slots ([TAI] "The KV cache":
+ * each step computes K/V only for the new token and caches them; [IR]
+ * "PagedAttention...": a table maps logical positions to physical slots).
+ * k_src, v_src  [num_tokens][n_kv_heads][d_head] of dtype (either may be NULL)
+ * slot_mapping  int64 [num_tokens]: slot = block * 16 + offset; a negative
+ *               slot skips the token; slots >= num_blocks*16 are skipped
+ * k_pool, v_pool  pools with kv_bits = 32 (PA_F32) or 16 (PA_BF16), written
+ * ------------------------------------------------------------------------ */
+int paged_kv_write(const void* k_src, const void* v_src, const int64_t* slot_mapping, int num_tokens,
+                   void* k_pool, void* v_pool, int num_blocks, int block_size,
+                   int n_kv_heads, int d_head, int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

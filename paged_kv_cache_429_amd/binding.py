@@ -1,0 +1,238 @@
+"""ctypes binding of libpagedattn.so (include/paged_attn.h).
+
+Argument marshalling only: every step of decode, prefill, quantization and
+cache writes runs in the library's HIP kernels. PyTorch supplies device
+memory and the current stream. There is no fallback: if the library is not
+built, or a tensor is not on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+
+PA_OK = 0
+PA_F32, PA_BF16 = 0, 1
+PA_KIND_K, PA_KIND_V = 0, 1
+BLOCK_SIZE = 16
+
+# every function declared in include/paged_attn.h
+EXPORTS = (
+    "pa_error_string", "pa_tile_bytes", "pa_kv_bytes_per_token", "pa_kv_cache_bytes",
+    "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_prefill_chunk",
+    "kv_quantize", "paged_kv_write",
+)
+
+_lib = None
+_lock = threading.Lock()
+
+
+class PagedAttnError(RuntimeError):
+    pass
+
+
+def _declare(lib):
+    i, sz, vp, u64, i64 = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int64
+    lib.pa_error_string.restype = ctypes.c_char_p
+    lib.pa_error_string.argtypes = [i]
+    lib.pa_tile_bytes.restype = sz
+    lib.pa_tile_bytes.argtypes = [i, i]
+    lib.pa_kv_bytes_per_token.restype = u64
+    lib.pa_kv_bytes_per_token.argtypes = [i, i, i, i]
+    lib.pa_kv_cache_bytes.restype = u64
+    lib.pa_kv_cache_bytes.argtypes = [i, i, i, i, i64]
+    lib.paged_attn_decode_workspace_size.restype = sz
+    lib.paged_attn_decode_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.paged_attn_decode.restype = i
+    lib.paged_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, i, i, i, vp, vp, sz, i, vp]
+    lib.paged_attn_prefill_chunk.restype = i
+    lib.paged_attn_prefill_chunk.argtypes = [vp, vp, i, i, vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, i, i, i,
+                                             vp, vp]
+    lib.kv_quantize.restype = i
+    lib.kv_quantize.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
+    lib.paged_kv_write.restype = i
+    lib.paged_kv_write.argtypes = [vp, vp, vp, i, vp, vp, i, i, i, i, i, vp]
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise PagedAttnError(f"{LIB_PATH} is missing: build it with "
+                                         "`python -m paged_kv_cache_429_amd.build`")
+                h = ctypes.CDLL(LIB_PATH)
+                _declare(h)
+                _lib = h
+    return _lib
+
+
+def _check(name, status):
+    if status != PA_OK:
+        msg = lib().pa_error_string(status).decode()
+        raise PagedAttnError(f"{name} failed: {msg} ({status})")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _gpu(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise PagedAttnError("tensors must be on a GPU")
+        if not t.is_contiguous():
+            raise PagedAttnError("tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise PagedAttnError("tensors must be on one device")
+    return dev
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(dt):
+    if dt == torch.float32:
+        return PA_F32
+    if dt == torch.bfloat16:
+        return PA_BF16
+    raise PagedAttnError(f"unsupported query dtype {dt}")
+
+
+def tile_bytes(d_head: int, kv_bits: int) -> int:
+    return int(lib().pa_tile_bytes(d_head, kv_bits))
+
+
+def kv_bytes_per_token(n_layers, n_kv_heads, d_head, kv_bits) -> int:
+    return int(lib().pa_kv_bytes_per_token(n_layers, n_kv_heads, d_head, kv_bits))
+
+
+def kv_cache_bytes(n_layers, n_kv_heads, d_head, kv_bits, n_tokens) -> int:
+    return int(lib().pa_kv_cache_bytes(n_layers, n_kv_heads, d_head, kv_bits, n_tokens))
+
+
+def alloc_pool(num_blocks, n_kv_heads, d_head, kv_bits, device="cuda"):
+    """Uninitialised pool in the library's tile layout (raw bytes)."""
+    return torch.empty((num_blocks, n_kv_heads, tile_bytes(d_head, kv_bits)), dtype=torch.uint8, device=device)
+
+
+def alloc_scales(num_blocks, n_kv_heads, device="cuda"):
+    return torch.empty((num_blocks, n_kv_heads), dtype=torch.float16, device=device)
+
+
+def _num_blocks(pool, n_kv, d, kv_bits):
+    per = n_kv * tile_bytes(d, kv_bits)
+    nbytes = pool.numel() * pool.element_size()
+    if per == 0 or nbytes % per:
+        raise PagedAttnError("pool size is not a whole number of blocks")
+    return nbytes // per
+
+
+_ws = {}
+
+
+def decode_workspace(num_seqs, n_heads, n_kv_heads, d_head, max_context_len, partition_blocks=0,
+                     device=None, stream=None):
+    """A workspace large enough for the call, cached per (device, stream).
+    Its contents never need initialising."""
+    n = int(lib().paged_attn_decode_workspace_size(num_seqs, n_heads, n_kv_heads, d_head, max_context_len,
+                                                   partition_blocks))
+    if n == 0:
+        return None
+    device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    key = (device.index, s.cuda_stream)
+    buf = _ws.get(key)
+    if buf is None or buf.numel() < n:
+        buf = torch.empty(max(n, 1 << 20), dtype=torch.uint8, device=device)
+        _ws[key] = buf
+    return buf
+
+
+def decode(q, k_pool, v_pool, block_tables, context_lens, *, n_kv_heads, max_context_len, kv_bits=None,
+           k_scales=None, v_scales=None, out=None, workspace=None, partition_blocks=0, stream=None):
+    """paged_attn_decode. q [S, H, D] (float32 or bfloat16); block_tables
+    [S, max_blocks] int32; context_lens [S] int32; returns out [S, H, D]."""
+    dev = _gpu(q, k_pool, v_pool, block_tables, context_lens, k_scales, v_scales, out, workspace)
+    S, H, D = q.shape
+    dt = _dtype_code(q.dtype)
+    if kv_bits is None:
+        kv_bits = 32 if dt == PA_F32 else 16
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise PagedAttnError("block_tables and context_lens must be int32")
+    nb = _num_blocks(k_pool, n_kv_heads, D, kv_bits)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = decode_workspace(S, H, n_kv_heads, D, max_context_len, partition_blocks, dev, stream)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().paged_attn_decode(
+        _p(q), _p(k_pool), _p(v_pool), _p(k_scales), _p(v_scales), _p(block_tables), block_tables.shape[1],
+        _p(context_lens), int(max_context_len), S, nb, BLOCK_SIZE, H, n_kv_heads, D, dt, kv_bits,
+        _p(out), _p(workspace), wbytes, int(partition_blocks), _stream(stream, dev))
+    _check("paged_attn_decode", st)
+    return out
+
+
+def prefill_chunk(q, cu_q_lens, k_pool, v_pool, block_tables, context_lens, *, n_kv_heads, max_q_len,
+                  max_context_len, kv_bits=None, k_scales=None, v_scales=None, out=None, stream=None):
+    """paged_attn_prefill_chunk. q [total_q, H, D]; cu_q_lens [S+1] int32."""
+    dev = _gpu(q, cu_q_lens, k_pool, v_pool, block_tables, context_lens, k_scales, v_scales, out)
+    T, H, D = q.shape
+    dt = _dtype_code(q.dtype)
+    if kv_bits is None:
+        kv_bits = 32 if dt == PA_F32 else 16
+    nb = _num_blocks(k_pool, n_kv_heads, D, kv_bits)
+    if out is None:
+        out = torch.empty_like(q)
+    S = context_lens.shape[0]
+    st = lib().paged_attn_prefill_chunk(
+        _p(q), _p(cu_q_lens), T, int(max_q_len), _p(k_pool), _p(v_pool), _p(k_scales), _p(v_scales),
+        _p(block_tables), block_tables.shape[1], _p(context_lens), int(max_context_len), S, nb, BLOCK_SIZE,
+        H, n_kv_heads, D, dt, kv_bits, _p(out), _stream(stream, dev))
+    _check("paged_attn_prefill_chunk", st)
+    return out
+
+
+def quantize(src_pool, *, bits, kind, n_kv_heads, d_head, codes=None, scales=None, block_ids=None, stream=None):
+    """kv_quantize of a bf16 pool; returns (codes pool, fp16 scales)."""
+    dev = _gpu(src_pool, codes, scales, block_ids)
+    nb = _num_blocks(src_pool, n_kv_heads, d_head, 16)
+    if codes is None:
+        codes = alloc_pool(nb, n_kv_heads, d_head, bits, dev)
+    if scales is None:
+        scales = alloc_scales(nb, n_kv_heads, dev)
+    n_ids = 0 if block_ids is None else block_ids.numel()
+    st = lib().kv_quantize(_p(src_pool), _p(codes), _p(scales), _p(block_ids), n_ids, nb, n_kv_heads, BLOCK_SIZE,
+                           d_head, bits, kind, _stream(stream, dev))
+    _check("kv_quantize", st)
+    return codes, scales
+
+
+def kv_write(k_src, v_src, slot_mapping, k_pool, v_pool, *, n_kv_heads, stream=None):
+    """paged_kv_write: k_src/v_src [T, n_kv, D] float32 or bfloat16; slot_mapping [T] int64."""
+    src = k_src if k_src is not None else v_src
+    dev = _gpu(k_src, v_src, slot_mapping, k_pool, v_pool)
+    T, _, D = src.shape
+    dt = _dtype_code(src.dtype)
+    if slot_mapping.dtype != torch.int64:
+        raise PagedAttnError("slot_mapping must be int64")
+    kv_bits = 32 if dt == PA_F32 else 16
+    nb = _num_blocks(k_pool if k_pool is not None else v_pool, n_kv_heads, D, kv_bits)
+    st = lib().paged_kv_write(_p(k_src), _p(v_src), _p(slot_mapping), T, _p(k_pool), _p(v_pool), nb, BLOCK_SIZE,
+                              n_kv_heads, D, dt, _stream(stream, dev))
+    _check("paged_kv_write", st)

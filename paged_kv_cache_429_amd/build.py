@@ -1,0 +1,71 @@
+"""Build libpagedattn.so (gfx950) in-tree with hipcc.
+
+    python -m paged_kv_cache_429_amd.build [-v]
+
+Every HIP source is compiled with
+  --offload-arch=gfx950 -O3 -Xclang -target-feature -Xclang -packed-fp32-ops
+(no packed-fp32 VALU instructions are generated; the host pass warns that it
+does not know the feature, which is harmless).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libpagedattn.so")
+SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "kvops.hip"]
+ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found (set HIPCC)")
+
+
+def _flags():
+    return [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include")]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(line for line in r.stdout.splitlines() if "packed-fp32-ops" not in line)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link the shared library; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    cc = hipcc()
+    objs = []
+    cmds = []
+    for s in SOURCES:
+        o = os.path.join(BUILD, os.path.splitext(s)[0] + ".o")
+        objs.append(o)
+        lang = ["-x", "hip"] if s.endswith(".hip") else []
+        cmds.append([cc] + _flags() + lang + ["-c", os.path.join(CSRC, s), "-o", o])
+    with ThreadPoolExecutor(min(len(cmds), 8)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,234 @@
+// C-ABI entry points: argument validation, split planning and launch.
+// Every check runs on the host before any device work is enqueued.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdint>
+#include <cmath>
+
+#include "../../include/paged_attn.h"
+#include "pa_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// Compute units of the current device (cached per device; 256 on MI355X).
+int cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int v = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+int fmt_of(int dtype, int kv_bits) {
+    if (dtype == PA_F32 && kv_bits == 32) return 0;
+    if (dtype == PA_BF16 && kv_bits == 16) return 1;
+    if (dtype == PA_BF16 && kv_bits == 8) return 2;
+    if (dtype == PA_BF16 && kv_bits == 4) return 3;
+    return -1;
+}
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Blocks per partition. Depends only on host-side shape arguments (never on
+// device data or physical block ids), so a given set of arguments always
+// splits every sequence at the same logical positions.
+int plan_partition_blocks(int num_seqs, int n_kv, int max_context_len, int requested) {
+    if (requested > 0) return requested;
+    const int max_blocks = std::max(1, ceil_div(max_context_len, PA_BLOCK_SIZE));
+    const long target = 4L * cu_count();  // workgroups wanted in flight
+    int pb = 64;
+    while (pb > 8) {
+        const long units = (long)num_seqs * n_kv * ceil_div(max_blocks, pb);
+        if (units >= target) break;
+        pb /= 2;
+    }
+    return pb;
+}
+
+bool valid_common(int num_seqs, int num_blocks, int block_size, int n_heads, int n_kv_heads, int d_head) {
+    if (num_seqs < 0 || num_blocks <= 0 || n_heads <= 0 || n_kv_heads <= 0 || d_head <= 0) return false;
+    if (block_size != PA_BLOCK_SIZE) return false;
+    if (n_heads % n_kv_heads != 0) return false;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_error_string(int status) {
+    switch (status) {
+        case PA_OK: return "ok";
+        case PA_ERR_INVALID_ARG: return "invalid argument";
+        case PA_ERR_UNSUPPORTED: return "unsupported shape or format";
+        case PA_ERR_WORKSPACE: return "workspace missing or too small";
+        case PA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+size_t pa_tile_bytes(int d_head, int kv_bits) {
+    if (d_head <= 0 || (kv_bits != 32 && kv_bits != 16 && kv_bits != 8 && kv_bits != 4)) return 0;
+    return (size_t)PA_BLOCK_SIZE * d_head * kv_bits / 8;
+}
+
+uint64_t pa_kv_bytes_per_token(int n_layers, int n_kv_heads, int d_head, int kv_bits) {
+    if (n_layers <= 0 || n_kv_heads <= 0 || d_head <= 0 || kv_bits <= 0) return 0;
+    return 2ull * n_layers * n_kv_heads * (uint64_t)d_head * kv_bits / 8;
+}
+
+uint64_t pa_kv_cache_bytes(int n_layers, int n_kv_heads, int d_head, int kv_bits, int64_t n_tokens) {
+    if (n_layers <= 0 || n_kv_heads <= 0 || d_head <= 0 || n_tokens < 0) return 0;
+    if (kv_bits != 32 && kv_bits != 16 && kv_bits != 8 && kv_bits != 4) return 0;
+    const uint64_t blocks = (uint64_t)((n_tokens + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE);
+    const uint64_t tile = (uint64_t)PA_BLOCK_SIZE * d_head * kv_bits / 8 + (kv_bits < 16 ? 2 : 0);
+    return 2ull * n_layers * blocks * n_kv_heads * tile;
+}
+
+size_t paged_attn_decode_workspace_size(int num_seqs, int n_heads, int n_kv_heads, int d_head,
+                                        int max_context_len, int partition_blocks) {
+    if (num_seqs <= 0 || n_heads <= 0 || n_kv_heads <= 0 || d_head <= 0 || max_context_len <= 0) return 0;
+    if (partition_blocks < 0 || partition_blocks > 64 || (partition_blocks & 1)) return 0;
+    const int pb = plan_partition_blocks(num_seqs, n_kv_heads, max_context_len, partition_blocks);
+    const int pmax = ceil_div(ceil_div(max_context_len, PA_BLOCK_SIZE), pb);
+    return pa::decode_workspace_bytes(num_seqs, n_heads, d_head, pmax);
+}
+
+int paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
+                      const uint16_t* k_scales, const uint16_t* v_scales,
+                      const int32_t* block_tables, int max_blocks_per_seq,
+                      const int32_t* context_lens, int max_context_len,
+                      int num_seqs, int num_blocks, int block_size,
+                      int n_heads, int n_kv_heads, int d_head, int dtype, int kv_bits,
+                      void* out, void* workspace, size_t workspace_bytes,
+                      int partition_blocks, void* stream) {
+    if (!valid_common(num_seqs, num_blocks, block_size, n_heads, n_kv_heads, d_head)) return PA_ERR_INVALID_ARG;
+    if (max_blocks_per_seq <= 0 || max_context_len < 0) return PA_ERR_INVALID_ARG;
+    if (partition_blocks < 0 || partition_blocks > 64 || (partition_blocks & 1)) return PA_ERR_INVALID_ARG;
+    const int fmt = fmt_of(dtype, kv_bits);
+    if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID_ARG;
+    if (kv_bits != 32 && kv_bits != 16 && kv_bits != 8 && kv_bits != 4) return PA_ERR_INVALID_ARG;
+    if (fmt < 0) return PA_ERR_UNSUPPORTED;
+    if (d_head != 64 && d_head != 128) return PA_ERR_UNSUPPORTED;
+    const int G = n_heads / n_kv_heads;
+    if (G > PA_MAX_GROUP) return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PA_OK;
+    if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return PA_ERR_INVALID_ARG;
+    if (kv_bits < 16 && (!k_scales || !v_scales)) return PA_ERR_INVALID_ARG;
+    if (max_context_len == 0) max_context_len = 1;  // every row is then 0 or 1 token
+
+    pa::DecodeParams p{};
+    p.q = q;
+    p.k_pool = k_pool;
+    p.v_pool = v_pool;
+    p.k_scales = k_scales;
+    p.v_scales = v_scales;
+    p.tables = block_tables;
+    p.ctx = context_lens;
+    p.out = out;
+    p.max_blocks = max_blocks_per_seq;
+    p.ctx_cap = (int)std::min<long>((long)max_context_len, (long)PA_BLOCK_SIZE * max_blocks_per_seq);
+    p.num_seqs = num_seqs;
+    p.num_blocks = num_blocks;
+    p.n_heads = n_heads;
+    p.n_kv = n_kv_heads;
+    p.group = G;
+    // planned from max_context_len exactly as paged_attn_decode_workspace_size() does
+    p.pb = plan_partition_blocks(num_seqs, n_kv_heads, std::max(1, max_context_len), partition_blocks);
+    p.pmax = ceil_div(ceil_div(p.ctx_cap, PA_BLOCK_SIZE), p.pb);
+    p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d_head));
+
+    const size_t need = pa::decode_workspace_bytes(num_seqs, n_heads, d_head, p.pmax);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+        pa::decode_workspace_carve(workspace, num_seqs, n_heads, d_head, p.pmax, &p.part_acc, &p.part_ml);
+    }
+    const hipError_t e = pa::launch_decode(p, d_head, fmt, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int paged_attn_prefill_chunk(const void* q, const int32_t* cu_q_lens, int total_q, int max_q_len,
+                             const void* k_pool, const void* v_pool,
+                             const uint16_t* k_scales, const uint16_t* v_scales,
+                             const int32_t* block_tables, int max_blocks_per_seq,
+                             const int32_t* context_lens, int max_context_len,
+                             int num_seqs, int num_blocks, int block_size,
+                             int n_heads, int n_kv_heads, int d_head, int dtype, int kv_bits,
+                             void* out, void* stream) {
+    if (!valid_common(num_seqs, num_blocks, block_size, n_heads, n_kv_heads, d_head)) return PA_ERR_INVALID_ARG;
+    if (max_blocks_per_seq <= 0 || max_context_len < 0 || total_q < 0 || max_q_len < 0) return PA_ERR_INVALID_ARG;
+    if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID_ARG;
+    if (kv_bits != 32 && kv_bits != 16 && kv_bits != 8 && kv_bits != 4) return PA_ERR_INVALID_ARG;
+    const int fmt = fmt_of(dtype, kv_bits);
+    if (fmt < 0) return PA_ERR_UNSUPPORTED;
+    if (d_head != 64 && d_head != 128) return PA_ERR_UNSUPPORTED;
+    const int G = n_heads / n_kv_heads;
+    if (G > PA_MAX_GROUP) return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
+    if (!q || !cu_q_lens || !k_pool || !v_pool || !block_tables || !context_lens || !out) return PA_ERR_INVALID_ARG;
+    if (kv_bits < 16 && (!k_scales || !v_scales)) return PA_ERR_INVALID_ARG;
+
+    pa::PrefillParams p{};
+    p.q = q;
+    p.cu_q_lens = cu_q_lens;
+    p.k_pool = k_pool;
+    p.v_pool = v_pool;
+    p.k_scales = k_scales;
+    p.v_scales = v_scales;
+    p.tables = block_tables;
+    p.ctx = context_lens;
+    p.out = out;
+    p.max_blocks = max_blocks_per_seq;
+    p.ctx_cap = (int)std::min<long>((long)max_context_len, (long)PA_BLOCK_SIZE * max_blocks_per_seq);
+    p.num_seqs = num_seqs;
+    p.num_blocks = num_blocks;
+    p.n_heads = n_heads;
+    p.n_kv = n_kv_heads;
+    p.group = G;
+    p.max_q_len = max_q_len;
+    p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d_head));
+    const hipError_t e = pa::launch_prefill(p, d_head, fmt, static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int kv_quantize(const void* src, void* codes, uint16_t* scales, const int32_t* block_ids, int n_ids,
+                int num_blocks, int n_kv_heads, int block_size, int d_head, int bits, int kind, void* stream) {
+    if (num_blocks <= 0 || n_kv_heads <= 0 || block_size != PA_BLOCK_SIZE || d_head <= 0) return PA_ERR_INVALID_ARG;
+    if (bits != 8 && bits != 4) return PA_ERR_INVALID_ARG;
+    if (kind != PA_KIND_K && kind != PA_KIND_V) return PA_ERR_INVALID_ARG;
+    if (d_head != 64 && d_head != 128) return PA_ERR_UNSUPPORTED;
+    if (block_ids && n_ids < 0) return PA_ERR_INVALID_ARG;
+    const int n = block_ids ? n_ids : num_blocks;
+    if (n == 0) return PA_OK;
+    if (!src || !codes || !scales) return PA_ERR_INVALID_ARG;
+    const hipError_t e = pa::launch_quantize(src, codes, scales, block_ids, n, num_blocks, n_kv_heads, d_head, bits,
+                                             kind, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int paged_kv_write(const void* k_src, const void* v_src, const int64_t* slot_mapping, int num_tokens,
+                   void* k_pool, void* v_pool, int num_blocks, int block_size,
+                   int n_kv_heads, int d_head, int dtype, void* stream) {
+    if (num_tokens < 0 || num_blocks <= 0 || block_size != PA_BLOCK_SIZE || n_kv_heads <= 0 || d_head <= 0)
+        return PA_ERR_INVALID_ARG;
+    if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID_ARG;
+    if (d_head != 64 && d_head != 128) return PA_ERR_UNSUPPORTED;
+    if (num_tokens == 0 || (!k_src && !v_src)) return PA_OK;
+    if (!slot_mapping) return PA_ERR_INVALID_ARG;
+    if ((k_src && !k_pool) || (v_src && !v_pool)) return PA_ERR_INVALID_ARG;
+    const hipError_t e = pa::launch_kv_write(k_src, v_src, slot_mapping, num_tokens, k_pool, v_pool, num_blocks,
+                                             n_kv_heads, d_head, dtype == PA_F32 ? 0 : 1,
+                                             static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,154 @@
+// Paged decode attention for gfx950.
+//
+// What is computed ("KV cache, continuous batching and paged attention",
+// section "Paged attention": the attention kernel follows the block table):
+// for every sequence s and query head h,
+//     o[s,h] = softmax(q[s,h] . K_s^T / sqrt(d)) V_s
+// where K_s / V_s are the context_lens[s] cached tokens of KV head h / G,
+// found through the sequence's block table.
+//
+// Work decomposition. One workgroup (4 waves) per (sequence, KV head,
+// context partition). A partition is `pb` consecutive logical blocks; the
+// waves take pairs of blocks round-robin. All G query heads of the KV head
+// are processed together, so each K/V tile is read from HBM once per KV head
+// (GQA batching, "KV cache, GQA, paging and continuous batching", section
+// "What it is"). Waves keep an online softmax (running max m, running sum l,
+// unnormalised accumulator), merge through LDS, and either write the output
+// (single partition) or a partial (m, l, acc) to the workspace; the last
+// workgroup of a (sequence, KV head) to finish merges the partials with a
+// log-sum-exp reduction and resets its arrival counter.
+//
+// MFMA formulation (bf16 / int8 / int4 KV). Per pair of blocks:
+//   S^T[32 tok x 16 col] = K[tok x d] * Q^T[d x col]   (2 x D/32 MFMA 16x16x32)
+//   O^T[d x col]        += V^T[d x 32 tok] * P^T[32 tok x col] (D/16 MFMA)
+// The 16 columns are the G query heads of the KV head (zero-padded). With
+// the K tile stored in 16-byte chunks of consecutive dims (slot-minor) and
+// the V tile stored transposed, every lane's MFMA operand is a contiguous
+// 16-byte (K) or 8-byte (V) load, and each wave load instruction reads a
+// contiguous 1 KiB (K) or 512 B (V) run. The S^T accumulator layout (lane
+// holds 4 consecutive tokens of one column) is exactly the B-operand layout
+// the P*V product needs, so probabilities never cross lanes.
+//
+// fp32 KV uses a plain VALU path with the same decomposition and epilogue.
+#include "pa_attn.h"
+
+namespace pa {
+
+template <int D, int FMT>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
+    __shared__ WaveState<D> st;
+    Unit u;
+    const int unit = blockIdx.x;
+    u.kvh = unit % p.n_kv;
+    const int rest = unit / p.n_kv;
+    u.part = rest % p.pmax;
+    u.s = rest / p.pmax;
+    u.ctx = min(p.ctx[u.s], p.ctx_cap);
+    constexpr bool F32OUT = (FMT == FMT_F32);
+    if (u.ctx <= 0) {
+        if (u.part == 0) {
+            for (int idx = threadIdx.x; idx < p.group * D; idx += kThreads)
+                store_out<D, F32OUT>(p, ((size_t)u.s * p.n_heads + u.kvh * p.group) * D + idx, 0.f);
+        }
+        return;
+    }
+    u.nblk = (u.ctx + kBlock - 1) / kBlock;
+    u.nparts = (u.nblk + p.pb - 1) / p.pb;
+    if (u.part >= u.nparts) return;
+    u.b_begin = u.part * p.pb;
+    u.b_end = min(u.nblk, u.b_begin + p.pb);
+
+    const int32_t* trow = p.tables + (size_t)u.s * p.max_blocks;
+    if constexpr (FMT == FMT_F32) {
+        __shared__ float qs[16 * D];
+        const float* qg = reinterpret_cast<const float*>(p.q) + ((size_t)u.s * p.n_heads + u.kvh * p.group) * D;
+        for (int idx = threadIdx.x; idx < p.group * D; idx += kThreads) qs[idx] = qg[idx];
+        __syncthreads();
+        f32_wave<D>(p, u, trow, st, qs);
+    } else {
+        const int my_id = load_ids(trow, u.b_begin, u.b_end - u.b_begin, p.num_blocks);
+        mfma_wave<D, FMT>(p, u, my_id, st);
+    }
+    epilogue<D, F32OUT>(p, u, st);
+}
+
+// Log-sum-exp merge of the partition partials of every (sequence, KV head)
+// with more than one partition (single-partition rows were written by the
+// partition kernel). m and l are in log2 units:
+//   M = max_p m_p,  o = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M)
+template <int D, bool F32OUT>
+__global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
+    const int s = blockIdx.x / p.n_kv;
+    const int kvh = blockIdx.x - s * p.n_kv;
+    const int ctx = min(p.ctx[s], p.ctx_cap);
+    if (ctx <= 0) return;
+    const int nparts = ((ctx + kBlock - 1) / kBlock + p.pb - 1) / p.pb;
+    if (nparts <= 1) return;
+    const int G = p.group;
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+        const int g = idx / D, d = idx - g * D;
+        const size_t h = (size_t)s * p.n_heads + kvh * G + g;
+        const float* ml = p.part_ml + h * p.pmax * 2;
+        const float* acc = p.part_acc + h * p.pmax * D + d;
+        float M = kNegInf;
+        for (int pp = 0; pp < nparts; ++pp) M = fmaxf(M, ml[2 * pp]);
+        float L = 0.f, O = 0.f;
+        for (int pp = 0; pp < nparts; ++pp) {
+            const float e = __builtin_amdgcn_exp2f(ml[2 * pp] - M);
+            L += e * ml[2 * pp + 1];
+            O += e * acc[(size_t)pp * D];
+        }
+        store_out<D, F32OUT>(p, h * D + d, O / L);
+    }
+}
+
+size_t decode_workspace_bytes(int num_seqs, int n_heads, int d, int pmax) {
+    if (pmax <= 1) return 0;
+    const size_t rows = (size_t)num_seqs * n_heads * pmax;
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    return al(rows * d * sizeof(float)) + al(rows * 2 * sizeof(float));
+}
+
+void decode_workspace_carve(void* ws, int num_seqs, int n_heads, int d, int pmax, float** part_acc,
+                            float** part_ml) {
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t rows = (size_t)num_seqs * n_heads * pmax;
+    char* b = static_cast<char*>(ws);
+    *part_acc = reinterpret_cast<float*>(b);
+    b += al(rows * d * sizeof(float));
+    *part_ml = reinterpret_cast<float*>(b);
+}
+
+template <int D, int FMT>
+static hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
+    const size_t grid = (size_t)p.num_seqs * p.pmax * p.n_kv;
+    if (grid == 0) return hipSuccess;
+    if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((decode_kernel<D, FMT>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.pmax <= 1) return e;
+    hipLaunchKernelGGL((merge_kernel<D, FMT == FMT_F32>), dim3((unsigned)(p.num_seqs * p.n_kv)), dim3(kThreads), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeParams& p, int d, int fmt, hipStream_t stream) {
+    if (d == 128) {
+        switch (fmt) {
+            case FMT_F32: return launch_t<128, FMT_F32>(p, stream);
+            case FMT_BF16: return launch_t<128, FMT_BF16>(p, stream);
+            case FMT_I8: return launch_t<128, FMT_I8>(p, stream);
+            case FMT_I4: return launch_t<128, FMT_I4>(p, stream);
+        }
+    } else if (d == 64) {
+        switch (fmt) {
+            case FMT_F32: return launch_t<64, FMT_F32>(p, stream);
+            case FMT_BF16: return launch_t<64, FMT_BF16>(p, stream);
+            case FMT_I8: return launch_t<64, FMT_I8>(p, stream);
+            case FMT_I4: return launch_t<64, FMT_I4>(p, stream);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pa

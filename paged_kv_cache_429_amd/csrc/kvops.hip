@@ -1,0 +1,170 @@
+// Cache-side kernels for gfx950: symmetric int8/int4 quantization of a bf16
+// pool, and scattering new tokens' K/V into their slots.
+//
+// Quantization ("jovanaeducation" inference guide a2-inf-2, section
+// "KV-cache quantization": every key/value is an integer sharing one scale
+// with its group). Group = one (block, KV head) tile of 16 slots x d dims:
+//   s = fp16_rne(amax / qmax), code = clamp(rint(x / float(s)), -qmax, qmax)
+// with IEEE float32 division and round-half-to-even (v_rndne_f32).
+//
+// Slot writes ("KV cache, continuous batching and paged attention", section
+// "The KV cache": each step computes K/V only for the new token and caches
+// them) follow the pool layout: K tiles in 16-byte chunks of consecutive dims
+// (slot-minor), V tiles transposed (dim-major).
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+// element number of (slot t, dim i) inside a K tile, x elements per 16 bytes
+__device__ __forceinline__ int k_elem(int t, int i, int x) { return ((i / x) * 16 + t) * x + i % x; }
+
+template <int D, int BITS, int KIND>
+__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ src, uint8_t* __restrict__ codes,
+                                                      uint16_t* __restrict__ scales, const int32_t* __restrict__ ids,
+                                                      int n_ids, int num_blocks, int n_kv) {
+    const int lane = threadIdx.x & 63;
+    const long tile = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (tile >= (long)n_ids * n_kv) return;
+    const int i_id = (int)(tile / n_kv);
+    const int h = (int)(tile % n_kv);
+    const int b = ids ? ids[i_id] : i_id;
+    if ((unsigned)b >= (unsigned)num_blocks) return;
+    constexpr int N = 16 * D;
+    const uint16_t* t = src + ((size_t)b * n_kv + h) * N;
+
+    float amax = 0.f;
+    for (int e = lane; e < N; e += 64) amax = fmaxf(amax, fabsf(bf16_bits_to_f32(t[e])));
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+
+    constexpr float qmax = (BITS == 8) ? 127.f : 7.f;
+    const float s32 = amax / qmax;                 // IEEE division
+    const _Float16 s16 = (_Float16)s32;            // round to nearest even
+    const float sf = (float)s16;
+    if (lane == 0) scales[(size_t)b * n_kv + h] = __builtin_bit_cast(uint16_t, s16);
+    const bool zero = !(sf > 0.f);                 // s == 0: all codes 0
+
+    auto code_of = [&](int n) -> int {
+        // element n of the int tile -> (slot, dim) -> source element
+        int tt, ii;
+        if (KIND == 0) {
+            constexpr int x = 128 / BITS;
+            const int c = n / (16 * x);
+            tt = (n / x) % 16;
+            ii = c * x + n % x;
+        } else {
+            ii = n / 16;
+            tt = n % 16;
+        }
+        const int se = (KIND == 0) ? k_elem(tt, ii, 8) : ii * 16 + tt;
+        if (zero) return 0;
+        const float r = bf16_bits_to_f32(t[se]) / sf;
+        float c = __builtin_rintf(r);
+        c = fminf(fmaxf(c, -qmax), qmax);
+        return (int)c;
+    };
+
+    uint8_t* out = codes + ((size_t)b * n_kv + h) * (N * BITS / 8);
+    for (int o = lane; o < N * BITS / 8; o += 64) {
+        if (BITS == 8) {
+            out[o] = (uint8_t)(int8_t)code_of(o);
+        } else {
+            const int lo = code_of(2 * o) & 0xf;
+            const int hi = code_of(2 * o + 1) & 0xf;
+            out[o] = (uint8_t)(lo | (hi << 4));
+        }
+    }
+}
+
+template <int D, int BITS, int KIND>
+static hipError_t quant_t(const void* src, void* codes, uint16_t* scales, const int32_t* ids, int n_ids,
+                          int num_blocks, int n_kv, hipStream_t stream) {
+    const long tiles = (long)n_ids * n_kv;
+    if (tiles == 0) return hipSuccess;
+    const long grid = (tiles + 3) / 4;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((quantize_kernel<D, BITS, KIND>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(src), static_cast<uint8_t*>(codes), scales, ids, n_ids,
+                       num_blocks, n_kv);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void* src, void* codes, uint16_t* scales, const int32_t* block_ids, int n_ids,
+                           int num_blocks, int n_kv, int d, int bits, int kind, hipStream_t stream) {
+#define PA_Q(DD, BB, KK) \
+    if (d == DD && bits == BB && kind == KK) \
+        return quant_t<DD, BB, KK>(src, codes, scales, block_ids, n_ids, num_blocks, n_kv, stream);
+    PA_Q(128, 8, 0) PA_Q(128, 8, 1) PA_Q(128, 4, 0) PA_Q(128, 4, 1)
+    PA_Q(64, 8, 0) PA_Q(64, 8, 1) PA_Q(64, 4, 0) PA_Q(64, 4, 1)
+#undef PA_Q
+    return hipErrorInvalidValue;
+}
+
+// One thread per (token, KV head, 16-byte chunk of the source row).
+template <int D, int EB>
+__global__ __launch_bounds__(256) void kv_write_kernel(const uint8_t* __restrict__ ksrc,
+                                                      const uint8_t* __restrict__ vsrc,
+                                                      const int64_t* __restrict__ slots, int ntok,
+                                                      uint8_t* __restrict__ kpool, uint8_t* __restrict__ vpool,
+                                                      int num_blocks, int n_kv) {
+    constexpr int CH = D * EB / 16;   // chunks per row
+    constexpr int X = 16 / EB;        // elements per chunk
+    constexpr size_t TILE = (size_t)16 * D * EB;
+    const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+    const long total = (long)ntok * n_kv * CH;
+    if (gid >= total) return;
+    const int c = (int)(gid % CH);
+    const int h = (int)((gid / CH) % n_kv);
+    const long tok = gid / ((long)CH * n_kv);
+    const int64_t slot = slots[tok];
+    if (slot < 0 || slot >= (int64_t)num_blocks * 16) return;
+    const int64_t b = slot / 16;
+    const int t = (int)(slot % 16);
+    const size_t tile = ((size_t)b * n_kv + h) * TILE;
+    const size_t src = ((size_t)tok * n_kv + h) * D * EB + (size_t)c * 16;
+    if (ksrc) {
+        *reinterpret_cast<u32x4*>(kpool + tile + (size_t)(c * 16 + t) * 16) =
+            *reinterpret_cast<const u32x4*>(ksrc + src);
+    }
+    if (vsrc) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(vsrc + src);
+        const uint8_t* vb = reinterpret_cast<const uint8_t*>(&v);
+#pragma unroll
+        for (int e = 0; e < X; ++e) {
+            const int i = c * X + e;
+            uint8_t* dst = vpool + tile + (size_t)(i * 16 + t) * EB;
+            if (EB == 2) {
+                *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(vb + 2 * e);
+            } else {
+                *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(vb + 4 * e);
+            }
+        }
+    }
+}
+
+template <int D, int EB>
+static hipError_t write_t(const void* k_src, const void* v_src, const int64_t* slots, int ntok, void* kp, void* vp,
+                          int num_blocks, int n_kv, hipStream_t stream) {
+    const long total = (long)ntok * n_kv * (D * EB / 16);
+    if (total == 0) return hipSuccess;
+    const long grid = (total + 255) / 256;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((kv_write_kernel<D, EB>), dim3((unsigned)grid), dim3(256), 0, stream,
+                       static_cast<const uint8_t*>(k_src), static_cast<const uint8_t*>(v_src), slots, ntok,
+                       static_cast<uint8_t*>(kp), static_cast<uint8_t*>(vp), num_blocks, n_kv);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_write(const void* k_src, const void* v_src, const int64_t* slots, int num_tokens,
+                           void* k_pool, void* v_pool, int num_blocks, int n_kv, int d, int fmt,
+                           hipStream_t stream) {
+    const int eb = (fmt == FMT_F32) ? 4 : 2;
+    if (d == 128 && eb == 2) return write_t<128, 2>(k_src, v_src, slots, num_tokens, k_pool, v_pool, num_blocks, n_kv, stream);
+    if (d == 128 && eb == 4) return write_t<128, 4>(k_src, v_src, slots, num_tokens, k_pool, v_pool, num_blocks, n_kv, stream);
+    if (d == 64 && eb == 2) return write_t<64, 2>(k_src, v_src, slots, num_tokens, k_pool, v_pool, num_blocks, n_kv, stream);
+    if (d == 64 && eb == 4) return write_t<64, 4>(k_src, v_src, slots, num_tokens, k_pool, v_pool, num_blocks, n_kv, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pa

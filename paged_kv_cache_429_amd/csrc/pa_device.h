@@ -1,0 +1,93 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, bf16/fp16
+// conversions, MFMA wrappers and wave reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 16;   // tokens per physical block
+constexpr int kWave = 64;    // CDNA wavefront
+
+enum KvFmt { FMT_F32 = 0, FMT_BF16 = 1, FMT_I8 = 2, FMT_I4 = 3 };
+
+template <int FMT> struct FmtBits;
+template <> struct FmtBits<FMT_F32> { static constexpr int v = 32; };
+template <> struct FmtBits<FMT_BF16> { static constexpr int v = 16; };
+template <> struct FmtBits<FMT_I8> { static constexpr int v = 8; };
+template <> struct FmtBits<FMT_I4> { static constexpr int v = 4; };
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> bfloat16 bits, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float fp16_bits_to_f32(uint16_t h) {
+    _Float16 x = __builtin_bit_cast(_Float16, h);
+    return (float)x;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D(16x16 f32) += A(16x32 bf16) * B(32x16 bf16). Lane l supplies row l%16 of
+// A and column l%16 of B, eight consecutive k each (k-slot group l/16); the
+// result lane l holds rows 4*(l/16)+i, column l%16.
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Exact int8 -> bf16 of the four codes in a dword (|code| <= 128 fits bf16).
+__device__ __forceinline__ u32x2 i8x4_to_bf16x4(uint32_t w) {
+    float f0 = (float)((int32_t)(w << 24) >> 24);
+    float f1 = (float)((int32_t)(w << 16) >> 24);
+    float f2 = (float)((int32_t)(w << 8) >> 24);
+    float f3 = (float)((int32_t)w >> 24);
+    u32x2 r;
+    r[0] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+    r[1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u);
+    return r;
+}
+
+// Exact int4 -> bf16 of the eight nibbles of a dword (low nibble first).
+__device__ __forceinline__ u32x4 i4x8_to_bf16x8(uint32_t w) {
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float lo = (float)((int32_t)(w << (28 - 8 * k)) >> 28);
+        float hi = (float)((int32_t)(w << (24 - 8 * k)) >> 28);
+        r[k] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+    }
+    return r;
+}
+
+// Exact int4 -> bf16 of the four nibbles in the low 16 bits.
+__device__ __forceinline__ u32x2 i4x4_to_bf16x4(uint32_t w) {
+    u32x4 t = i4x8_to_bf16x8(w);
+    u32x2 r;
+    r[0] = t[0];
+    r[1] = t[1];
+    return r;
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask)); }
+
+template <typename T>
+__device__ __forceinline__ T readlane(T v, int lane) {
+    return __builtin_amdgcn_readlane(v, lane);
+}
+
+}  // namespace pa

@@ -1,0 +1,72 @@
+// Host <-> kernel interface of the library (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct DecodeParams {
+    const void* q;
+    const void* k_pool;
+    const void* v_pool;
+    const uint16_t* k_scales;
+    const uint16_t* v_scales;
+    const int32_t* tables;
+    const int32_t* ctx;
+    void* out;
+    float* part_acc;    // [num_seqs][n_heads][pmax][d]   (unnormalised)
+    float* part_ml;     // [num_seqs][n_heads][pmax][2]   (max, sum) in log2 units
+    int max_blocks;     // table row stride
+    int ctx_cap;        // min(max_context_len, 16 * max_blocks)
+    int num_seqs;
+    int num_blocks;
+    int n_heads;
+    int n_kv;
+    int group;
+    int pmax;           // partitions per sequence at max_context_len
+    int pb;             // blocks per partition (even)
+    float scale_log2;   // log2(e) / sqrt(d)
+};
+
+// Workspace bytes for the split-context partials (0 when pmax == 1).
+size_t decode_workspace_bytes(int num_seqs, int n_heads, int d, int pmax);
+void decode_workspace_carve(void* ws, int num_seqs, int n_heads, int d, int pmax, float** part_acc,
+                            float** part_ml);
+
+// fmt: 0 fp32, 1 bf16, 2 int8, 3 int4. Launches the partition kernel and,
+// when pmax > 1, the merge kernel, on `stream`.
+hipError_t launch_decode(const DecodeParams& p, int d, int fmt, hipStream_t stream);
+
+struct PrefillParams {
+    const void* q;
+    const int32_t* cu_q_lens;
+    const void* k_pool;
+    const void* v_pool;
+    const uint16_t* k_scales;
+    const uint16_t* v_scales;
+    const int32_t* tables;
+    const int32_t* ctx;
+    void* out;
+    int max_blocks;
+    int ctx_cap;
+    int num_seqs;
+    int num_blocks;
+    int n_heads;
+    int n_kv;
+    int group;
+    int max_q_len;
+    float scale_log2;
+};
+
+hipError_t launch_prefill(const PrefillParams& p, int d, int fmt, hipStream_t stream);
+
+hipError_t launch_quantize(const void* src, void* codes, uint16_t* scales, const int32_t* block_ids, int n_ids,
+                           int num_blocks, int n_kv, int d, int bits, int kind, hipStream_t stream);
+
+hipError_t launch_kv_write(const void* k_src, const void* v_src, const int64_t* slots, int num_tokens,
+                           void* k_pool, void* v_pool, int num_blocks, int n_kv, int d, int fmt,
+                           hipStream_t stream);
+
+}  // namespace pa
