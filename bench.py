@@ -39,6 +39,10 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode attention: achieved HBM GB/s (% of peak) and decode tokens/s per layer"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+# counter summaries under profiles/ (name of the kernel and workload)
+PROFILE_NAME = {"2": "decode_kernel_llama3_8b_bf16", "3": "decode_kernel_prefix_shared_70b_bf16",
+                "4a": "decode_kernel_quant_kv_70b_int8", "4b": "decode_kernel_quant_kv_70b_int4",
+                "5d": "decode_kernel_mixed_step_decode_bf16"}
 
 
 def parse():
@@ -51,7 +55,63 @@ def parse():
     ap.add_argument("--partition-blocks", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="instead of the benchmark, run a plain device copy of this many MiB (calibrates "
+                         "the HBM byte counters) and print its size and time")
     return ap.parse_args()
+
+
+def copy_probe(mib, reps):
+    """A plain device-to-device copy of a known size: FETCH_SIZE / WRITE_SIZE
+    read on it give the factor between those counters and real bytes."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        t.append((a, b))
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in t]))
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "reps": reps,
+                      "median_ms": round(ms, 4), "copy_GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
+def kernel_source_hash():
+    """sha256 (first 16 hex digits) of the library's kernel sources, the key
+    under which profiles/*.hbm.md records counter-measured traffic."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "paged_kv_cache_429_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(profile):
+    """HBM bytes per launch from a committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, scaled by the copy calibration), or None when the summary is
+    missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", profile + ".hbm.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "source_hash"):
+                k, v = line.split(":", 1)
+                vals[k] = v.strip()
+    if vals.get("source_hash") != kernel_source_hash() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return int(vals["traffic_bytes_per_launch"])
 
 
 def decode_bytes(case, kv_bits):
@@ -140,6 +200,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if a.copy_probe_mib:
+        copy_probe(a.copy_probe_mib, max(1, a.steps))
+        return
     t_gen = time.perf_counter()
     case, kv_bits = build_case(a.workload)
     gen_s = time.perf_counter() - t_gen
@@ -223,7 +286,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(PROFILE_NAME[a.workload]),
             "kernel_avg_us": round(k_avg * 1e3, 3),
             "kernel_p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
             "kernel_p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 3),
