@@ -97,6 +97,7 @@ typedef enum pa_kv_kind { PA_KIND_K = 0, PA_KIND_V = 1 } pa_kv_kind;
 
 #define PA_BLOCK_SIZE 16
 #define PA_MAX_GROUP 16
+#define PA_DECODE_COUNTER_BYTES (1u << 20)
 
 /* Human-readable text of a status code (static storage). */
 const char* pa_error_string(int status);
@@ -131,15 +132,21 @@ uint64_t pa_kv_cache_bytes(int n_layers, int n_kv_heads, int d_head, int kv_bits
  * max_context_len  host-side upper bound of context_lens (plans the split)
  * out          [num_seqs][n_heads][d_head] of dtype (written)
  * workspace    device scratch of at least paged_attn_decode_workspace_size()
- *              bytes (may be NULL when that size is 0): the partials of
- *              split sequences. Its contents on entry do not matter. Calls
- *              that share a workspace must be ordered (same stream, or
- *              synchronised); overlapping calls on one workspace race.
+ *              bytes (may be NULL when that size is 0). Its first
+ *              PA_DECODE_COUNTER_BYTES hold arrival counters, one int32 per
+ *              (sequence, KV head), so num_seqs * n_kv_heads may not exceed
+ *              PA_DECODE_COUNTER_BYTES / 4 (else PA_ERR_UNSUPPORTED). The
+ *              counters must be zero before the first call that uses the
+ *              workspace (allocate it zero-filled); every call that completes
+ *              leaves them zero again. The rest holds the partials of split
+ *              sequences and needs no initialisation. One workspace serves
+ *              calls of any shape, but calls that share it must be ordered
+ *              (same stream, or synchronised): overlapping calls race.
  * partition_blocks  blocks per context partition (even, 2..64), or 0 to let
  *              the library choose. Long contexts are split into partitions
- *              processed in parallel and merged by log-sum-exp in a second
- *              kernel on the same stream (launched only when some sequence
- *              can span more than one partition); the split depends only on
+ *              processed in parallel and merged by log-sum-exp within the
+ *              same launch: the last partition of a (sequence, KV head) to
+ *              finish merges them, in partition order. The split depends only on
  *              the arguments' values on the host and on each sequence's
  *              length, never on physical block ids.
  * ------------------------------------------------------------------------ */

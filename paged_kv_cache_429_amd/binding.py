@@ -148,7 +148,8 @@ _ws = {}
 def decode_workspace(num_seqs, n_heads, n_kv_heads, d_head, max_context_len, partition_blocks=0,
                      device=None, stream=None):
     """A workspace large enough for the call, cached per (device, stream).
-    Its contents never need initialising."""
+    It is allocated zero-filled: its leading arrival counters must start at
+    zero, and every completed call leaves them zero."""
     n = int(lib().paged_attn_decode_workspace_size(num_seqs, n_heads, n_kv_heads, d_head, max_context_len,
                                                    partition_blocks))
     if n == 0:
@@ -158,7 +159,7 @@ def decode_workspace(num_seqs, n_heads, n_kv_heads, d_head, max_context_len, par
     key = (device.index, s.cuda_stream)
     buf = _ws.get(key)
     if buf is None or buf.numel() < n:
-        buf = torch.empty(max(n, 1 << 20), dtype=torch.uint8, device=device)
+        buf = torch.zeros(max(n, 2 << 20), dtype=torch.uint8, device=device)
         _ws[key] = buf
     return buf
 

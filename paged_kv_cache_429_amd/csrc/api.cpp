@@ -99,7 +99,7 @@ size_t paged_attn_decode_workspace_size(int num_seqs, int n_heads, int n_kv_head
     if (partition_blocks < 0 || partition_blocks > 64 || (partition_blocks & 1)) return 0;
     const int pb = plan_partition_blocks(num_seqs, n_kv_heads, max_context_len, partition_blocks);
     const int pmax = ceil_div(ceil_div(max_context_len, PA_BLOCK_SIZE), pb);
-    return pa::decode_workspace_bytes(num_seqs, n_heads, d_head, pmax);
+    return pa::decode_workspace_bytes(num_seqs, n_heads, n_kv_heads, d_head, pmax);
 }
 
 int paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
@@ -146,10 +146,12 @@ int paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
     p.pmax = ceil_div(ceil_div(p.ctx_cap, PA_BLOCK_SIZE), p.pb);
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d_head));
 
-    const size_t need = pa::decode_workspace_bytes(num_seqs, n_heads, d_head, p.pmax);
+    const size_t need = pa::decode_workspace_bytes(num_seqs, n_heads, n_kv_heads, d_head, p.pmax);
     if (need > 0) {
+        if ((long)num_seqs * n_kv_heads > pa::kMaxCounterPairs) return PA_ERR_UNSUPPORTED;
         if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
-        pa::decode_workspace_carve(workspace, num_seqs, n_heads, d_head, p.pmax, &p.part_acc, &p.part_ml);
+        pa::decode_workspace_carve(workspace, num_seqs, n_heads, n_kv_heads, d_head, p.pmax, &p.part_acc, &p.part_ml,
+                                   &p.counters);
     }
     const hipError_t e = pa::launch_decode(p, d_head, fmt, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;

@@ -8,7 +8,9 @@
 // found through the sequence's block table.
 //
 // Work decomposition. One workgroup (4 waves) per (sequence, KV head,
-// context partition). A partition is `pb` consecutive logical blocks; the
+// context partition); the KV head is the fastest-varying index, so with 8 KV
+// heads each head's workgroups land on one XCD (workgroups are dealt to the
+// 8 XCDs round-robin). A partition is `pb` consecutive logical blocks; the
 // waves take pairs of blocks round-robin. All G query heads of the KV head
 // are processed together, so each K/V tile is read from HBM once per KV head
 // (GQA batching, "KV cache, GQA, paging and continuous batching", section
@@ -16,7 +18,8 @@
 // unnormalised accumulator), merge through LDS, and either write the output
 // (single partition) or a partial (m, l, acc) to the workspace; the last
 // workgroup of a (sequence, KV head) to finish merges the partials with a
-// log-sum-exp reduction and resets its arrival counter.
+// log-sum-exp reduction in partition order and re-arms its arrival counter,
+// so one launch does the whole step.
 //
 // MFMA formulation (bf16 / int8 / int4 KV). Per pair of blocks:
 //   S^T[32 tok x 16 col] = K[tok x d] * Q^T[d x col]   (2 x D/32 MFMA 16x16x32)
@@ -34,8 +37,16 @@
 
 namespace pa {
 
+// Waves per SIMD the register budget is sized for: the bf16 loop fits three
+// (<= 168 VGPRs); the int8/int4 dequantisation needs more registers.
+template <int FMT>
+constexpr int decode_waves_per_eu() {
+    return FMT == FMT_BF16 ? 3 : 2;
+}
+
 template <int D, int FMT>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<FMT>())))
+void decode_kernel(DecodeParams p) {
     __shared__ WaveState<D> st;
     Unit u;
     const int unit = blockIdx.x;
@@ -72,50 +83,28 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     epilogue<D, F32OUT>(p, u, st);
 }
 
-// Log-sum-exp merge of the partition partials of every (sequence, KV head)
-// with more than one partition (single-partition rows were written by the
-// partition kernel). m and l are in log2 units:
-//   M = max_p m_p,  o = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M)
-template <int D, bool F32OUT>
-__global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
-    const int s = blockIdx.x / p.n_kv;
-    const int kvh = blockIdx.x - s * p.n_kv;
-    const int ctx = min(p.ctx[s], p.ctx_cap);
-    if (ctx <= 0) return;
-    const int nparts = ((ctx + kBlock - 1) / kBlock + p.pb - 1) / p.pb;
-    if (nparts <= 1) return;
-    const int G = p.group;
-    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-        const int g = idx / D, d = idx - g * D;
-        const size_t h = (size_t)s * p.n_heads + kvh * G + g;
-        const float* ml = p.part_ml + h * p.pmax * 2;
-        const float* acc = p.part_acc + h * p.pmax * D + d;
-        float M = kNegInf;
-        for (int pp = 0; pp < nparts; ++pp) M = fmaxf(M, ml[2 * pp]);
-        float L = 0.f, O = 0.f;
-        for (int pp = 0; pp < nparts; ++pp) {
-            const float e = __builtin_amdgcn_exp2f(ml[2 * pp] - M);
-            L += e * ml[2 * pp + 1];
-            O += e * acc[(size_t)pp * D];
-        }
-        store_out<D, F32OUT>(p, h * D + d, O / L);
-    }
-}
+// Workspace: a fixed-size region of arrival counters at offset 0, then the
+// partial accumulators and (max, sum) pairs. Because the counter region
+// never moves or shrinks, calls of any shape can share one workspace: the
+// counters stay zero between calls and partial data never lands on them.
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t decode_workspace_bytes(int num_seqs, int n_heads, int d, int pmax) {
+size_t decode_workspace_bytes(int num_seqs, int n_heads, int n_kv, int d, int pmax) {
+    (void)n_kv;
     if (pmax <= 1) return 0;
     const size_t rows = (size_t)num_seqs * n_heads * pmax;
-    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    return al(rows * d * sizeof(float)) + al(rows * 2 * sizeof(float));
+    return kCounterBytes + align256(rows * d * sizeof(float)) + align256(rows * 2 * sizeof(float));
 }
 
-void decode_workspace_carve(void* ws, int num_seqs, int n_heads, int d, int pmax, float** part_acc,
-                            float** part_ml) {
-    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+void decode_workspace_carve(void* ws, int num_seqs, int n_heads, int n_kv, int d, int pmax, float** part_acc,
+                            float** part_ml, int** counters) {
+    (void)n_kv;
     const size_t rows = (size_t)num_seqs * n_heads * pmax;
     char* b = static_cast<char*>(ws);
+    *counters = reinterpret_cast<int*>(b);
+    b += kCounterBytes;
     *part_acc = reinterpret_cast<float*>(b);
-    b += al(rows * d * sizeof(float));
+    b += align256(rows * d * sizeof(float));
     *part_ml = reinterpret_cast<float*>(b);
 }
 
@@ -125,10 +114,6 @@ static hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
     if (grid == 0) return hipSuccess;
     if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((decode_kernel<D, FMT>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.pmax <= 1) return e;
-    hipLaunchKernelGGL((merge_kernel<D, FMT == FMT_F32>), dim3((unsigned)(p.num_seqs * p.n_kv)), dim3(kThreads), 0,
-                       stream, p);
     return hipGetLastError();
 }
 

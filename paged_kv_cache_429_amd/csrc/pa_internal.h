@@ -18,6 +18,7 @@ struct DecodeParams {
     void* out;
     float* part_acc;    // [num_seqs][n_heads][pmax][d]   (unnormalised)
     float* part_ml;     // [num_seqs][n_heads][pmax][2]   (max, sum) in log2 units
+    int* counters;      // [num_seqs][n_kv] partitions arrived (zero between calls)
     int max_blocks;     // table row stride
     int ctx_cap;        // min(max_context_len, 16 * max_blocks)
     int num_seqs;
@@ -30,13 +31,19 @@ struct DecodeParams {
     float scale_log2;   // log2(e) / sqrt(d)
 };
 
-// Workspace bytes for the split-context partials (0 when pmax == 1).
-size_t decode_workspace_bytes(int num_seqs, int n_heads, int d, int pmax);
-void decode_workspace_carve(void* ws, int num_seqs, int n_heads, int d, int pmax, float** part_acc,
-                            float** part_ml);
+// Bytes of the arrival-counter region at the start of a decode workspace:
+// one int32 per (sequence, KV head), so num_seqs * n_kv_heads <= 262144.
+constexpr size_t kCounterBytes = (size_t)1 << 20;
+constexpr long kMaxCounterPairs = (long)(kCounterBytes / sizeof(int));
 
-// fmt: 0 fp32, 1 bf16, 2 int8, 3 int4. Launches the partition kernel and,
-// when pmax > 1, the merge kernel, on `stream`.
+// Workspace bytes for the arrival counters and split-context partials (0
+// when pmax == 1).
+size_t decode_workspace_bytes(int num_seqs, int n_heads, int n_kv, int d, int pmax);
+void decode_workspace_carve(void* ws, int num_seqs, int n_heads, int n_kv, int d, int pmax, float** part_acc,
+                            float** part_ml, int** counters);
+
+// fmt: 0 fp32, 1 bf16, 2 int8, 3 int4. Launches the decode kernel on
+// `stream`.
 hipError_t launch_decode(const DecodeParams& p, int d, int fmt, hipStream_t stream);
 
 struct PrefillParams {

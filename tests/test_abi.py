@@ -79,6 +79,14 @@ def test_decode_rejects_on_host(B, over, code):
     assert _decode(B, **over) == code
 
 
+def test_decode_counter_capacity(B):
+    """One int32 arrival counter per (sequence, KV head) lives in a fixed
+    1 MiB region: larger split batches are rejected on the host."""
+    ws = 1 << 40  # never dereferenced: the call returns before any device work
+    assert _decode(B, ns=262144 // 8 + 1, Hkv=8, H=32, mb=256, mcl=4096, ws=ws, wsb=1 << 40) == -2
+    assert _decode(B, ns=262144 // 8 + 1, Hkv=8, H=32, mb=256, mcl=4096, ws=None, wsb=0) == -2
+
+
 def test_decode_empty_batch_is_noop(B):
     assert _decode(B, ns=0, q=None, out=None) == 0
 
@@ -89,7 +97,7 @@ def test_workspace_size(B):
     n = L.paged_attn_decode_workspace_size(4, 8, 2, 128, 4096, 16)          # 16 partitions
     rows = 4 * 8 * 16
     al = lambda x: (x + 255) // 256 * 256
-    assert n == al(rows * 128 * 4) + al(rows * 2 * 4)
+    assert n == (1 << 20) + al(rows * 128 * 4) + al(rows * 2 * 4)   # counters, partial acc, (m, l)
     assert L.paged_attn_decode_workspace_size(4, 8, 2, 128, 4096, 3) == 0   # invalid partition size
 
 
