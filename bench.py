@@ -1,6 +1,6 @@
 """Benchmark: paged decode attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|3|4a|4b|5d|5p] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|3|4a|4b|5d|5p|5] [--no-cpu-baseline]
 
 A step is one paged_attn_decode call (all G query heads of every KV head,
 every sequence of the batch, split-context merge included) over one layer's
@@ -189,6 +189,118 @@ def cpu_baseline(case, kv_bits, budget_s):
     }
 
 
+def prefill_flops(c):
+    """4 d flops (Q.K and P.V) per (query head, visible key) pair of the chunk."""
+    total = 0
+    for s in range(c.num_seqs):
+        qlen = int(c.cu_q_lens[s + 1] - c.cu_q_lens[s])
+        n = int(c.context_lens[s])
+        pos = n - qlen + np.arange(qlen, dtype=np.int64)
+        total += int((pos + 1).sum())
+    return 4 * c.d * c.n_heads * total
+
+
+def prefill_cpu_baseline(c, budget_s):
+    """The oracle on chunk rows spread over the chunk (whole rows, all heads)
+    until about `budget_s` seconds; GFLOP/s over the same flop count."""
+    import oracle
+    q = oracle.as_f64(c.q, c.dtype)
+    kf, vf = oracle.as_f64(c.k_slots, c.dtype), oracle.as_f64(c.v_slots, c.dtype)
+    qlen = int(c.cu_q_lens[1] - c.cu_q_lens[0])
+    order = np.random.default_rng(0).permutation(qlen)
+    done = []
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 <= budget_s and len(done) < qlen:
+        r = [int(x) for x in order[len(done):len(done) + 16]]
+        oracle.paged_prefill(q, c.cu_q_lens, kf, vf, c.block_tables, c.context_lens, n_kv=c.n_kv, rows=r)
+        done.extend(r)
+    el = time.perf_counter() - t0
+    pos = int(c.context_lens[0]) - qlen + np.asarray(done, dtype=np.int64)
+    fl = 4 * c.d * c.n_heads * int((pos + 1).sum())
+    return {"value": round(fl / el / 1e9, 3), "unit": "GFLOP/s", "cores": _CORES, "kind": "oracle",
+            "sample": f"{len(done)} of {qlen} chunk rows (all heads, causal) in {el:.1f} s; float64 NumPy"}
+
+
+def prefill_main(a, torch, B, CONFIGS):
+    """Workload 5: the 2048-token causal chunk over 6000 cached tokens alone
+    ('5p'), or the whole mixed step ('5': the chunk on one stream and the 64
+    decodes on a second, both bracketed by events on the first)."""
+    from synth import make_mixed_case
+    pre, dec = make_mixed_case()
+    kp = B.alloc_pool(pre.num_blocks, pre.n_kv, pre.d, 16)
+    vp = B.alloc_pool(pre.num_blocks, pre.n_kv, pre.d, 16)
+    slots = torch.arange(pre.num_blocks * 16, dtype=torch.int64, device="cuda")
+    B.kv_write(to_dev(pre.k_slots, "bf16", torch), to_dev(pre.v_slots, "bf16", torch), slots, kp, vp,
+               n_kv_heads=pre.n_kv)
+    qp = to_dev(pre.q, "bf16", torch)
+    cu = torch.from_numpy(pre.cu_q_lens.astype(np.int32)).cuda()
+    tp = torch.from_numpy(np.ascontiguousarray(pre.block_tables)).cuda()
+    cp = torch.from_numpy(pre.context_lens.astype(np.int32)).cuda()
+    op = torch.empty_like(qp)
+    qd = to_dev(dec.q, "bf16", torch)
+    td = torch.from_numpy(np.ascontiguousarray(dec.block_tables)).cuda()
+    cd = torch.from_numpy(dec.context_lens.astype(np.int32)).cuda()
+    od = torch.empty_like(qd)
+    mixed = a.workload == "5"
+    s_main = torch.cuda.current_stream()
+    s_dec = torch.cuda.Stream() if mixed else None
+    ws = B.decode_workspace(dec.num_seqs, dec.n_heads, dec.n_kv, dec.d, dec.max_context_len, 0,
+                            stream=s_dec) if mixed else None
+    torch.cuda.synchronize()
+
+    def step():
+        B.prefill_chunk(qp, cu, kp, vp, tp, cp, n_kv_heads=pre.n_kv, max_q_len=pre.max_q_len,
+                        max_context_len=pre.max_context_len, out=op, stream=s_main)
+        if mixed:
+            s_dec.wait_stream(s_main)
+            B.decode(qd, kp, vp, td, cd, n_kv_heads=dec.n_kv, max_context_len=dec.max_context_len, out=od,
+                     workspace=ws, stream=s_dec)
+            s_main.wait_stream(s_dec)
+
+    def timed(n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            ev[i][0].record(s_main)
+            step()
+            ev[i][1].record(s_main)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, np.array([x.elapsed_time(y) for x, y in ev])
+
+    for _ in range(a.warmup):
+        step()
+    wall, kern_ms = timed(a.steps)
+    flops = prefill_flops(pre)
+    k_avg = float(kern_ms.mean())
+    ms_step = wall * 1e3 / a.steps
+    res = {
+        "metric": "causal chunked-prefill attention: achieved MFMA TFLOP/s (% of bf16 dense peak)"
+                  if not mixed else "mixed chunked-prefill step: step time, prefill TFLOP/s and decode GB/s",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2) if not mixed else round(ms_step * 1e3, 2),
+        "unit": "TFLOP/s" if not mixed else "us per step",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": not mixed, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": CONFIGS[5]["workload"] + (" [prefill chunk]" if not mixed else " [whole step]"),
+                   "chunk_tokens": pre.max_q_len, "context_tokens": int(pre.context_lens[0]),
+                   "n_heads": pre.n_heads, "n_kv_heads": pre.n_kv, "d_head": pre.d, "seed": pre.seed,
+                   "decode_seqs": dec.num_seqs if mixed else 0},
+        "flops_per_step": flops,
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel" if not mixed else "prefill_kernel+decode_kernel",
+                     "achieved": round(flops / (k_avg * 1e-3) / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(flops / (k_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel_avg_us": round(k_avg * 1e3, 3)},
+    }
+    if mixed:
+        res["decode_algorithmic_bytes"] = int(decode_bytes(dec, 16))
+        res["decode_tokens_per_s"] = round(dec.num_seqs / (ms_step * 1e-3), 1)
+        res["prefill_tokens_per_s"] = round(pre.max_q_len / (ms_step * 1e-3), 1)
+    if not a.no_cpu_baseline and not mixed:
+        res["cpu_baseline"] = prefill_cpu_baseline(pre, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -202,6 +314,9 @@ def main():
     torch.cuda.set_device(0)
     if a.copy_probe_mib:
         copy_probe(a.copy_probe_mib, max(1, a.steps))
+        return
+    if a.workload in ("5", "5p"):
+        prefill_main(a, torch, B, CONFIGS)
         return
     t_gen = time.perf_counter()
     case, kv_bits = build_case(a.workload)

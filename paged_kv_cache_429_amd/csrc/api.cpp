@@ -146,6 +146,20 @@ int paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
     p.pmax = ceil_div(ceil_div(p.ctx_cap, PA_BLOCK_SIZE), p.pb);
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d_head));
 
+    // Shared-prefix workgroups (groups of 16/G consecutive sequences whose
+    // tables name the same blocks fill the 16 MFMA columns) for the MFMA
+    // formats at G = 4 or 8, when sequences can be split.
+    p.share_n = 0;
+    p.n_shared = 0;
+    if (fmt != 0 && p.pmax > 1) {
+        p.share_n = (G == 4 || G == 8) ? 16 / G : 0;
+        if (p.share_n > 0) {
+            const long n = (long)(num_seqs / p.share_n) * p.pmax * n_kv_heads;
+            if (n > 0x3fffffffL) return PA_ERR_UNSUPPORTED;
+            p.n_shared = (int)n;
+            if (p.n_shared == 0) p.share_n = 0;
+        }
+    }
     const size_t need = pa::decode_workspace_bytes(num_seqs, n_heads, n_kv_heads, d_head, p.pmax);
     if (need > 0) {
         if ((long)num_seqs * n_kv_heads > pa::kMaxCounterPairs) return PA_ERR_UNSUPPORTED;

@@ -48,14 +48,20 @@ template <int D, int FMT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<FMT>())))
 void decode_kernel(DecodeParams p) {
     __shared__ WaveState<D> st;
+    constexpr bool F32OUT = (FMT == FMT_F32);
+    if constexpr (FMT != FMT_F32) {
+        if ((int)blockIdx.x < p.n_shared) {
+            shared_unit<D, FMT, 1, F32OUT>(p, blockIdx.x, st);
+            return;
+        }
+    }
     Unit u;
-    const int unit = blockIdx.x;
+    const int unit = blockIdx.x - p.n_shared;
     u.kvh = unit % p.n_kv;
     const int rest = unit / p.n_kv;
     u.part = rest % p.pmax;
     u.s = rest / p.pmax;
     u.ctx = min(p.ctx[u.s], p.ctx_cap);
-    constexpr bool F32OUT = (FMT == FMT_F32);
     if (u.ctx <= 0) {
         if (u.part == 0) {
             for (int idx = threadIdx.x; idx < p.group * D; idx += kThreads)
@@ -68,6 +74,10 @@ void decode_kernel(DecodeParams p) {
     if (u.part >= u.nparts) return;
     u.b_begin = u.part * p.pb;
     u.b_end = min(u.nblk, u.b_begin + p.pb);
+    if (p.share_n > 0) {  // taken by a shared-prefix workgroup?
+        const int grp = u.s / p.share_n;
+        if ((grp + 1) * p.share_n <= p.num_seqs && group_shares(p, grp * p.share_n, u.part)) return;
+    }
 
     const int32_t* trow = p.tables + (size_t)u.s * p.max_blocks;
     if constexpr (FMT == FMT_F32) {
@@ -110,7 +120,7 @@ void decode_workspace_carve(void* ws, int num_seqs, int n_heads, int n_kv, int d
 
 template <int D, int FMT>
 static hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
-    const size_t grid = (size_t)p.num_seqs * p.pmax * p.n_kv;
+    const size_t grid = (size_t)p.n_shared + (size_t)p.num_seqs * p.pmax * p.n_kv;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((decode_kernel<D, FMT>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);

@@ -6,6 +6,13 @@
 #include "pa_device.h"
 #include "pa_internal.h"
 
+// No floating-point contraction in the attention arithmetic: the same
+// source expression must round the same way wherever it is inlined (the
+// shared-prefix and per-sequence paths must agree bit for bit, and what the
+// compiler can prove about a mask would otherwise decide whether a multiply
+// and an add fuse).
+#pragma clang fp contract(off)
+
 namespace pa {
 
 constexpr int kWaves = 4;
@@ -49,16 +56,26 @@ struct Mfma {
     struct KRaw { uint32_t w[KDW]; };
     struct VRaw { uint32_t w[NB * VDW]; };
 
-    // Tile loads are nontemporal: decode streams every tile once, and the
-    // streaming hint lifts the 4 KiB-tile gather rate on gfx950 by ~12%.
-    // (The prefill kernel calls the same loaders on LDS, where the hint has
-    // no effect.)
+    // Tile loads are nontemporal by default: decode streams a private tile
+    // once, and the streaming hint lifts the 4 KiB-tile gather rate on gfx950
+    // by ~12%. Tiles that several workgroups read (shared prefix blocks) are
+    // loaded with the default, cache-friendly policy. (The prefill kernel
+    // calls the same loaders on LDS, where the hint has no effect.)
+    template <bool NT, typename T>
+    __device__ static __forceinline__ T ld(const T* a) {
+        if constexpr (NT) {
+            return __builtin_nontemporal_load(a);
+        } else {
+            return *a;
+        }
+    }
 
+    template <bool NT = true>
     __device__ static __forceinline__ void load_k(const uint8_t* tile, int lane, KRaw& r) {
         if (KDW >= 4) {
 #pragma unroll
             for (int u = 0; u < KDW / 4; ++u) {
-                u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tile + u * 1024 + lane * 16));
+                u32x4 v = ld<NT>(reinterpret_cast<const u32x4*>(tile + u * 1024 + lane * 16));
                 r.w[4 * u + 0] = v[0];
                 r.w[4 * u + 1] = v[1];
                 r.w[4 * u + 2] = v[2];
@@ -66,7 +83,7 @@ struct Mfma {
             }
         } else {  // int4, d = 64: half a 16-byte chunk per lane
             const int t = lane & 15, q = lane >> 4;
-            u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tile + (q >> 1) * 256 + t * 16 + (q & 1) * 8));
+            u32x2 v = ld<NT>(reinterpret_cast<const u32x2*>(tile + (q >> 1) * 256 + t * 16 + (q & 1) * 8));
             r.w[0] = v[0];
             r.w[1] = v[1];
         }
@@ -92,19 +109,20 @@ struct Mfma {
         return a;
     }
 
+    template <bool NT = true>
     __device__ static __forceinline__ void load_v(const uint8_t* tile, int lane, VRaw& r) {
         const int l16 = lane & 15, q = lane >> 4;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int d = nb * 16 + l16;
             if (FMT == FMT_BF16) {
-                u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tile + d * 32 + q * 8));
+                u32x2 v = ld<NT>(reinterpret_cast<const u32x2*>(tile + d * 32 + q * 8));
                 r.w[2 * nb] = v[0];
                 r.w[2 * nb + 1] = v[1];
             } else if (FMT == FMT_I8) {
-                r.w[nb] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(tile + d * 16 + q * 4));
+                r.w[nb] = ld<NT>(reinterpret_cast<const uint32_t*>(tile + d * 16 + q * 4));
             } else {
-                r.w[nb] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(tile + d * 8 + q * 2));
+                r.w[nb] = ld<NT>(reinterpret_cast<const uint16_t*>(tile + d * 8 + q * 2));
             }
         }
     }
@@ -140,154 +158,228 @@ struct VHalf {
     float s0, s1;
 };
 
+// Online-softmax state of the 16 MFMA columns of one wave: running max m and
+// sum l (log2 units; lane group q holds its partial sum) and the
+// unnormalised O^T accumulator.
+template <int D>
+struct ColState {
+    float m, l;
+    f32x4 acc[D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ void col_init(ColState<D>& c) {
+    c.m = kNegInf;
+    c.l = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) c.acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Every step below acts on each of the 16 columns independently (an MFMA
+// output element depends only on its own column of the B operand, and the
+// reductions run over the lane groups of one column), so a column's result
+// does not depend on what the other columns hold. The shared-prefix path
+// relies on this to reproduce the per-sequence path bit for bit.
+
+// S^T of a pair for the 16 query columns of qop: s0 holds tokens 4q..4q+3
+// of the first block, s1 those of the second.
+template <int D, int FMT>
+__device__ __forceinline__ void pair_scores(const KHalf<D, FMT>& r, const u32x4* qop, f32x4& s0, f32x4& s1) {
+    using M = Mfma<D, FMT>;
+    s0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    s1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < M::KSTEPS; ++kk) {
+        s0 = mfma_16x16x32(M::k_operand(r.k0, kk), qop[kk], s0);
+        s1 = mfma_16x16x32(M::k_operand(r.k1, kk), qop[kk], s1);
+    }
+}
+
+// Scores in log2 units (c0, c1 fold 1/sqrt(d), log2 e and the K scales),
+// masked by select: tokens at or past ctx, and a missing second block, get
+// -inf. tok0 is the lane's first token (pair start + 4q).
+__device__ __forceinline__ void scale_mask(const f32x4& s0, const f32x4& s1, float c0, float c1, int tok0, int ctx,
+                                           bool has1, float* x) {
+    const int tok1 = tok0 + kBlock;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[i] = (tok0 + i < ctx) ? s0[i] * c0 : kNegInf;
+        x[4 + i] = (has1 && tok1 + i < ctx) ? s1[i] * c1 : kNegInf;
+    }
+}
+
+// Online-softmax update of every column with one pair's scores; returns the
+// probabilities in pr. A column whose scores are all -inf is left unchanged.
+template <int D>
+__device__ __forceinline__ void softmax_update(ColState<D>& c, const float* x, float* pr) {
+    float mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
+    mx = wave_max_xor(mx, 16);
+    mx = wave_max_xor(mx, 32);
+    const float mnew = fmaxf(c.m, mx);
+    // While a column has seen no finite score its state stays zero (exp2 of
+    // -inf - 0); otherwise this is the usual rescale by 2^(m - mnew).
+    const float mref = (mnew == kNegInf) ? 0.f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(c.m - mref);
+    c.m = mnew;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(x[i] - mref);
+        psum += pr[i];
+    }
+    c.l = c.l * alpha + psum;
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) c.acc[nb] *= alpha;
+}
+
+// O^T += V^T P^T for one pair. t0 is the pair's first token; V slots at or
+// past ctx (and a missing second block) are zeroed, since their contents may
+// be anything (0 * NaN = NaN). Columns with own == false contribute a zero
+// P column (their accumulator is unchanged).
+template <int D, int FMT>
+__device__ __forceinline__ void pv_update(ColState<D>& c, const VHalf<D, FMT>& r, const float* pr, int t0, int ctx,
+                                          bool has1, bool own) {
+    using M = Mfma<D, FMT>;
+    const int q = (threadIdx.x & 63) >> 4;
+    u32x4 pop;
+    pop[0] = pack_bf16x2(pr[0] * r.s0, pr[1] * r.s0);
+    pop[1] = pack_bf16x2(pr[2] * r.s0, pr[3] * r.s0);
+    pop[2] = pack_bf16x2(pr[4] * r.s1, pr[5] * r.s1);
+    pop[3] = pack_bf16x2(pr[6] * r.s1, pr[7] * r.s1);
+    if (!own) pop = u32x4{0u, 0u, 0u, 0u};
+    const int tok0 = t0 + 4 * q;
+    const int tok1 = tok0 + kBlock;
+    const bool tail = !has1 || t0 + 2 * kBlock > ctx;
+    uint32_t msk0[2] = {0xffffffffu, 0xffffffffu};
+    uint32_t msk1[2] = {0xffffffffu, 0xffffffffu};
+    if (tail) {
+#pragma unroll
+        for (int w2 = 0; w2 < 2; ++w2) {
+            const int ta = tok0 + 2 * w2, tb = tok1 + 2 * w2;
+            msk0[w2] = (ta < ctx ? 0x0000ffffu : 0u) | (ta + 1 < ctx ? 0xffff0000u : 0u);
+            msk1[w2] = (has1 && tb < ctx ? 0x0000ffffu : 0u) | (has1 && tb + 1 < ctx ? 0xffff0000u : 0u);
+        }
+    }
+#pragma unroll
+    for (int nb = 0; nb < M::NB; ++nb) {
+        const u32x2 a0 = M::v_half(r.v0, nb);
+        const u32x2 a1 = M::v_half(r.v1, nb);
+        u32x4 vop;
+        vop[0] = a0[0] & msk0[0];
+        vop[1] = a0[1] & msk0[1];
+        vop[2] = a1[0] & msk1[0];
+        vop[3] = a1[1] & msk1[1];
+        c.acc[nb] = mfma_16x16x32(vop, pop, c.acc[nb]);
+    }
+}
+
+// Write one wave's column states to LDS slot `wave` (row sums completed
+// over the four lane groups of each column).
+template <int D>
+__device__ __forceinline__ void col_to_lds(ColState<D>& c, WaveState<D>& st, int wave) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane & 15;
+    const int q = lane >> 4;
+    float l = c.l;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (q == 0) {
+        st.m[wave][g] = c.m;
+        st.l[wave][g] = l;
+    }
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.acc[wave][g][nb * 16 + 4 * q + i] = c.acc[nb][i];
+    }
+}
+
+template <int D, int FMT, bool NT = true>
+__device__ __forceinline__ void issue_k_pair(const DecodeParams& p, int kvh, int i0, int i1, KHalf<D, FMT>& r) {
+    using M = Mfma<D, FMT>;
+    const int lane = threadIdx.x & 63;
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k_pool);
+    M::template load_k<NT>(kbase + ((size_t)i0 * p.n_kv + kvh) * M::TILE, lane, r.k0);
+    M::template load_k<NT>(kbase + ((size_t)i1 * p.n_kv + kvh) * M::TILE, lane, r.k1);
+    r.s0 = r.s1 = 1.f;
+    if (FMT == FMT_I8 || FMT == FMT_I4) {
+        r.s0 = fp16_bits_to_f32(p.k_scales[(size_t)i0 * p.n_kv + kvh]);
+        r.s1 = fp16_bits_to_f32(p.k_scales[(size_t)i1 * p.n_kv + kvh]);
+    }
+}
+
+template <int D, int FMT, bool NT = true>
+__device__ __forceinline__ void issue_v_pair(const DecodeParams& p, int kvh, int i0, int i1, VHalf<D, FMT>& r) {
+    using M = Mfma<D, FMT>;
+    const int lane = threadIdx.x & 63;
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v_pool);
+    M::template load_v<NT>(vbase + ((size_t)i0 * p.n_kv + kvh) * M::TILE, lane, r.v0);
+    M::template load_v<NT>(vbase + ((size_t)i1 * p.n_kv + kvh) * M::TILE, lane, r.v1);
+    r.s0 = r.s1 = 1.f;
+    if (FMT == FMT_I8 || FMT == FMT_I4) {
+        r.s0 = fp16_bits_to_f32(p.v_scales[(size_t)i0 * p.n_kv + kvh]);
+        r.s1 = fp16_bits_to_f32(p.v_scales[(size_t)i1 * p.n_kv + kvh]);
+    }
+}
+
+// Q^T operand of column `col` (query head qh of sequence s), eight dims per
+// k-step; zero for an unused column.
+template <int D, int FMT>
+__device__ __forceinline__ void load_qop(const DecodeParams& p, int s, int qh, bool used, u32x4* qop) {
+    using M = Mfma<D, FMT>;
+    const int q = (threadIdx.x & 63) >> 4;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)s * p.n_heads + qh) * D;
+#pragma unroll
+    for (int kk = 0; kk < M::KSTEPS; ++kk) {
+        qop[kk] = used ? *reinterpret_cast<const u32x4*>(qrow + M::dbase(kk, q)) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// One wave of a (sequence, KV head, partition) workgroup: pairs wave,
+// wave + 4, ... of the partition, the G query heads of the KV head in
+// columns 0..G-1.
 template <int D, int FMT>
 __device__ __forceinline__ void mfma_wave(const DecodeParams& p, const Unit& u, int my_id, WaveState<D>& st) {
     using M = Mfma<D, FMT>;
-    constexpr bool QUANT = (FMT == FMT_I8 || FMT == FMT_I4);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane & 15;
     const int q = lane >> 4;
-    const int G = p.group;
-    const int H = p.n_heads;
 
-    // Q^T operand: column g = query head kvh*G + g, eight dims per k-step.
     u32x4 qop[M::KSTEPS];
-    {
-        const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)u.s * H + u.kvh * G + g) * D;
-#pragma unroll
-        for (int kk = 0; kk < M::KSTEPS; ++kk) {
-            if (g < G) {
-                qop[kk] = *reinterpret_cast<const u32x4*>(qrow + M::dbase(kk, q));
-            } else {
-                qop[kk] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-    }
+    load_qop<D, FMT>(p, u.s, u.kvh * p.group + g, g < p.group, qop);
+    ColState<D> cs;
+    col_init(cs);
 
-    float m = kNegInf;
-    float l = 0.f;
-    f32x4 acc[M::NB];
-#pragma unroll
-    for (int nb = 0; nb < M::NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k_pool);
-    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v_pool);
     const int nb_part = u.b_end - u.b_begin;
     const int npairs = (nb_part + 1) >> 1;
-
-    // byte offsets of the two tiles of pair k (a missing second block
+    // physical ids of the two blocks of pair k (a missing second block
     // repeats the first, which is then masked out)
-    auto tiles = [&](int k, size_t& t0, size_t& t1, int& i0, int& i1) {
-        const int j0 = 2 * k;
-        i0 = tile_id(p, my_id, j0);
-        i1 = (j0 + 1) < nb_part ? tile_id(p, my_id, j0 + 1) : i0;
-        t0 = ((size_t)i0 * p.n_kv + u.kvh) * M::TILE;
-        t1 = ((size_t)i1 * p.n_kv + u.kvh) * M::TILE;
+    auto ids = [&](int k, int& i0, int& i1) {
+        i0 = tile_id(p, my_id, 2 * k);
+        i1 = (2 * k + 1) < nb_part ? tile_id(p, my_id, 2 * k + 1) : i0;
     };
-    auto issue_k = [&](int k, KHalf<D, FMT>& r) {
-        size_t t0, t1;
-        int i0, i1;
-        tiles(k, t0, t1, i0, i1);
-        M::load_k(kbase + t0, lane, r.k0);
-        M::load_k(kbase + t1, lane, r.k1);
-        r.s0 = r.s1 = 1.f;
-        if (QUANT) {
-            r.s0 = fp16_bits_to_f32(p.k_scales[(size_t)i0 * p.n_kv + u.kvh]);
-            r.s1 = fp16_bits_to_f32(p.k_scales[(size_t)i1 * p.n_kv + u.kvh]);
-        }
-    };
-    auto issue_v = [&](int k, VHalf<D, FMT>& r) {
-        size_t t0, t1;
-        int i0, i1;
-        tiles(k, t0, t1, i0, i1);
-        M::load_v(vbase + t0, lane, r.v0);
-        M::load_v(vbase + t1, lane, r.v1);
-        r.s0 = r.s1 = 1.f;
-        if (QUANT) {
-            r.s0 = fp16_bits_to_f32(p.v_scales[(size_t)i0 * p.n_kv + u.kvh]);
-            r.s1 = fp16_bits_to_f32(p.v_scales[(size_t)i1 * p.n_kv + u.kvh]);
-        }
-    };
-
-    // S^T for pair k, scaled to log2 units and masked by select: x[0..3] are
-    // tokens 4q..4q+3 of the first block, x[4..7] those of the second.
-    auto qk = [&](int k, const KHalf<D, FMT>& r, float* x) {
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
-        f32x4 s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < M::KSTEPS; ++kk) {
-            s0 = mfma_16x16x32(M::k_operand(r.k0, kk), qop[kk], s0);
-            s1 = mfma_16x16x32(M::k_operand(r.k1, kk), qop[kk], s1);
-        }
-        const int tok0 = (u.b_begin + 2 * k) * kBlock + 4 * q;
-        const int tok1 = tok0 + kBlock;
+    auto step = [&](int k, const KHalf<D, FMT>& kr, const VHalf<D, FMT>& vr, bool prefetch, KHalf<D, FMT>& kn,
+                    VHalf<D, FMT>& vn) {
+        const int t0 = (u.b_begin + 2 * k) * kBlock;
         const bool has1 = 2 * k + 1 < nb_part;
-        const float c0 = p.scale_log2 * r.s0;
-        const float c1 = p.scale_log2 * r.s1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[i] = (tok0 + i < u.ctx) ? s0[i] * c0 : kNegInf;
-            x[4 + i] = (has1 && tok1 + i < u.ctx) ? s1[i] * c1 : kNegInf;
+        f32x4 s0, s1;
+        pair_scores<D, FMT>(kr, qop, s0, s1);
+        // (kn may be kr: take the K scales before the prefetch replaces them)
+        const float c0 = p.scale_log2 * kr.s0;
+        const float c1 = p.scale_log2 * kr.s1;
+        int n0 = 0, n1 = 0;
+        if (prefetch) {
+            ids(k + kWaves, n0, n1);
+            issue_k_pair<D, FMT>(p, u.kvh, n0, n1, kn);
         }
-    };
-
-    // online-softmax update with the scores of pair k; returns the
-    // probabilities (not yet scaled by the V scales) in pr
-    auto softmax = [&](const float* x, float* pr) {
-        float mx = x[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-        mx = wave_max_xor(mx, 16);
-        mx = wave_max_xor(mx, 32);
-        const float mnew = fmaxf(m, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-        m = mnew;
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            pr[i] = __builtin_amdgcn_exp2f(x[i] - mnew);
-            psum += pr[i];
-        }
-        l = l * alpha + psum;
-#pragma unroll
-        for (int nb = 0; nb < M::NB; ++nb) acc[nb] *= alpha;
-    };
-
-    auto pv = [&](int k, const VHalf<D, FMT>& r, const float* pr) {
-        u32x4 pop;
-        pop[0] = pack_bf16x2(pr[0] * r.s0, pr[1] * r.s0);
-        pop[1] = pack_bf16x2(pr[2] * r.s0, pr[3] * r.s0);
-        pop[2] = pack_bf16x2(pr[4] * r.s1, pr[5] * r.s1);
-        pop[3] = pack_bf16x2(pr[6] * r.s1, pr[7] * r.s1);
-        // Tokens past the context (and a missing second block) have weight 0,
-        // but their V slots may hold anything (0 * NaN = NaN): zero them.
-        const int j0 = 2 * k;
-        const bool has1 = j0 + 1 < nb_part;
-        const int tok0 = (u.b_begin + j0) * kBlock + 4 * q;
-        const int tok1 = tok0 + kBlock;
-        const bool tail = !has1 || (u.b_begin + j0 + 2) * kBlock > u.ctx;
-        uint32_t msk0[2] = {0xffffffffu, 0xffffffffu};
-        uint32_t msk1[2] = {0xffffffffu, 0xffffffffu};
-        if (tail) {
-#pragma unroll
-            for (int w2 = 0; w2 < 2; ++w2) {
-                const int ta = tok0 + 2 * w2, tb = tok1 + 2 * w2;
-                msk0[w2] = (ta < u.ctx ? 0x0000ffffu : 0u) | (ta + 1 < u.ctx ? 0xffff0000u : 0u);
-                msk1[w2] = (has1 && tb < u.ctx ? 0x0000ffffu : 0u) | (has1 && tb + 1 < u.ctx ? 0xffff0000u : 0u);
-            }
-        }
-#pragma unroll
-        for (int nb = 0; nb < M::NB; ++nb) {
-            const u32x2 a0 = M::v_half(r.v0, nb);
-            const u32x2 a1 = M::v_half(r.v1, nb);
-            u32x4 vop;
-            vop[0] = a0[0] & msk0[0];
-            vop[1] = a0[1] & msk0[1];
-            vop[2] = a1[0] & msk1[0];
-            vop[3] = a1[1] & msk1[1];
-            acc[nb] = mfma_16x16x32(vop, pop, acc[nb]);
-        }
+        float x[8], pr[8];
+        scale_mask(s0, s1, c0, c1, t0 + 4 * q, u.ctx, has1, x);
+        softmax_update(cs, x, pr);
+        pv_update<D, FMT>(cs, vr, pr, t0, u.ctx, has1, true);
+        if (prefetch) issue_v_pair<D, FMT>(p, u.kvh, n0, n1, vn);
     };
 
     // Waves take pairs wave, wave+4, ... In the steady loop the next pair
@@ -297,33 +389,14 @@ __device__ __forceinline__ void mfma_wave(const DecodeParams& p, const Unit& u, 
     if (k < npairs) {
         KHalf<D, FMT> kr;
         VHalf<D, FMT> vr;
-        issue_k(k, kr);
-        issue_v(k, vr);
-        float x[8], pr[8];
-        for (; k + kWaves < npairs; k += kWaves) {
-            qk(k, kr, x);
-            issue_k(k + kWaves, kr);
-            softmax(x, pr);
-            pv(k, vr, pr);
-            issue_v(k + kWaves, vr);
-        }
-        qk(k, kr, x);
-        softmax(x, pr);
-        pv(k, vr, pr);
+        int i0, i1;
+        ids(k, i0, i1);
+        issue_k_pair<D, FMT>(p, u.kvh, i0, i1, kr);
+        issue_v_pair<D, FMT>(p, u.kvh, i0, i1, vr);
+        for (; k + kWaves < npairs; k += kWaves) step(k, kr, vr, true, kr, vr);
+        step(k, kr, vr, false, kr, vr);
     }
-
-    // row sum over the four lane groups holding the same column
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    if (q == 0) {
-        st.m[wave][g] = m;
-        st.l[wave][g] = l;
-    }
-#pragma unroll
-    for (int nb = 0; nb < M::NB; ++nb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st.acc[wave][g][nb * 16 + 4 * q + i] = acc[nb][i];
-    }
+    col_to_lds(cs, st, wave);
 }
 
 // -----------------------------------------------------------------------------
@@ -525,33 +598,33 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& p, int s, int
     }
 }
 
-// Merge the waves' softmax states through LDS. A single-partition sequence
-// writes its output here. Otherwise the workgroup writes its partition's
-// partial (max, sum, unnormalised accumulator), and the last workgroup of
-// the (sequence, KV head) to arrive merges all partials and re-arms the
-// arrival counter (zero between calls).
-template <int D, bool F32OUT>
-__device__ __forceinline__ void epilogue(const DecodeParams& p, const Unit& u, WaveState<D>& st) {
-    __syncthreads();
-    const int G = p.group;
-    const int H = p.n_heads;
-    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
-        const int g = idx / D, d = idx - g * D;
-        float M = st.m[0][g];
+// Merge the waves' column states held in LDS (in wave order) for columns
+// 0..ncols-1 and store each column's result: the output row of a sequence
+// with one partition, else this partition's partial (max, sum,
+// unnormalised accumulator). info(col, s, qh, nparts) names the column's
+// sequence, query head and partition count.
+template <int D, bool F32OUT, typename Info>
+__device__ __forceinline__ void merge_waves_store(const DecodeParams& p, const WaveState<D>& st, int ncols, int part,
+                                                  Info info) {
+    for (int idx = threadIdx.x; idx < ncols * D; idx += kThreads) {
+        const int col = idx / D, d = idx - col * D;
+        float M = st.m[0][col];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, st.m[w][g]);
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, st.m[w][col]);
         float L = 0.f, O = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float e = __builtin_amdgcn_exp2f(st.m[w][g] - M);  // 0 for a wave without blocks
-            L += e * st.l[w][g];
-            O += e * st.acc[w][g][d];
+            const float e = __builtin_amdgcn_exp2f(st.m[w][col] - M);  // 0 for a wave without blocks
+            L += e * st.l[w][col];
+            O += e * st.acc[w][col][d];
         }
-        const size_t h = (size_t)u.s * H + u.kvh * G + g;
-        if (u.nparts == 1) {
+        int s, qh, nparts;
+        info(col, s, qh, nparts);
+        const size_t h = (size_t)s * p.n_heads + qh;
+        if (nparts == 1) {
             store_out<D, F32OUT>(p, h * D + d, O / L);
         } else {
-            const size_t row = h * p.pmax + u.part;
+            const size_t row = h * p.pmax + part;
             store_agent(p.part_acc + row * D + d, O);
             if (d == 0) {
                 store_agent(p.part_ml + row * 2, M);
@@ -559,6 +632,32 @@ __device__ __forceinline__ void epilogue(const DecodeParams& p, const Unit& u, W
             }
         }
     }
+}
+
+// Count one partition of (sequence s, KV head kvh) as arrived; true for the
+// last of its nparts partitions, which then re-arms the counter (zero
+// between calls). Called by one thread after every thread's partial stores
+// have reached the coherence point.
+__device__ __forceinline__ bool arrive(const DecodeParams& p, int s, int kvh, int nparts) {
+    int* cnt = p.counters + (size_t)s * p.n_kv + kvh;
+    const int before = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = (before == nparts - 1);
+    if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return last;
+}
+
+// Epilogue of a (sequence, KV head, partition) workgroup: merge the waves,
+// store, and if this was the last partition of a split sequence to arrive,
+// merge all its partials.
+template <int D, bool F32OUT>
+__device__ __forceinline__ void epilogue(const DecodeParams& p, const Unit& u, WaveState<D>& st) {
+    __syncthreads();
+    const int G = p.group;
+    merge_waves_store<D, F32OUT>(p, st, G, u.part, [&](int col, int& s, int& qh, int& np) {
+        s = u.s;
+        qh = u.kvh * G + col;
+        np = u.nparts;
+    });
     if (u.nparts == 1) return;
 
     __shared__ int last;
@@ -566,16 +665,226 @@ __device__ __forceinline__ void epilogue(const DecodeParams& p, const Unit& u, W
     // the workgroup's arrival is counted.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int* cnt = p.counters + (size_t)u.s * p.n_kv + u.kvh;
-        const int before = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = (before == u.nparts - 1);
-        // every other partition has arrived: re-arm the counter for the next call
-        if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (threadIdx.x == 0) last = arrive(p, u.s, u.kvh, u.nparts);
     __syncthreads();
     if (!last) return;
     merge_partials<D, F32OUT>(p, u.s, u.kvh, u.nparts);
+}
+
+// -----------------------------------------------------------------------------
+// Shared-prefix workgroups ("jovanaeducation" guide a2-inf-2, section "Prefix
+// caching"; "KV cache, GQA, paging and continuous batching", section
+// "PagedAttention...": sequences with a common prefix point their block
+// tables at the same physical blocks).
+//
+// A group of NS = 16/G consecutive sequences (G = 4 or 8) whose tables name
+// the same physical blocks for the first pair of a partition, all full, is
+// processed by one workgroup for that (KV head, partition): the G query
+// heads of the NS sequences fill the 16 MFMA columns (CS = 1 column set per
+// wave; the template allows more where registers permit). A block pair that every sequence
+// of the group shares (same ids, full in every sequence) is loaded once, with
+// the cache-friendly policy so that the other groups' workgroups find it in
+// L2, and feeds all columns; any other pair is loaded per sequence and feeds
+// only that sequence's columns (the others see a zero P column and -inf
+// scores, which leave their state unchanged). Pairs are visited in the same
+// wave-to-pair order as the per-sequence workgroups, and every column goes
+// through the same operations, so a sequence's result does not depend on
+// which kind of workgroup computed it: shared blocks give bit-identical
+// output to private copies of the same data.
+// -----------------------------------------------------------------------------
+constexpr int kMaxShareSeqs = 4;
+
+// Do the share_n sequences from s0 on all hold the first block pair of
+// partition `part`, full, at the same physical ids?
+__device__ __forceinline__ bool group_shares(const DecodeParams& p, int s0, int part) {
+    const int b = part * p.pb;
+    const int need = (b + 2) * kBlock;
+    for (int i = 0; i < p.share_n; ++i) {
+        if (min(p.ctx[s0 + i], p.ctx_cap) < need) return false;
+    }
+    const int32_t* t0 = p.tables + (size_t)s0 * p.max_blocks + b;
+    const int id0 = t0[0], id1 = t0[1];
+    for (int i = 1; i < p.share_n; ++i) {
+        const int32_t* ti = p.tables + (size_t)(s0 + i) * p.max_blocks + b;
+        if (ti[0] != id0 || ti[1] != id1) return false;
+    }
+    return true;
+}
+
+template <int D, int FMT, int CS, bool F32OUT>
+__device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, WaveState<D>& st) {
+    using M = Mfma<D, FMT>;
+    const int kvh = unit % p.n_kv;
+    const int rest = unit / p.n_kv;
+    const int part = rest % p.pmax;
+    const int grp = rest / p.pmax;
+    const int NS = p.share_n;
+    const int s0 = grp * NS;
+    if (!group_shares(p, s0, part)) return;
+
+    const int G = p.group;
+    const int TPG = 16 / G;  // sequences per column set
+    const int b = part * p.pb;
+    int ctx[kMaxShareSeqs], nbp[kMaxShareSeqs], npairs[kMaxShareSeqs], nparts[kMaxShareSeqs];
+    int npmax = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxShareSeqs; ++i) {
+        ctx[i] = (i < NS) ? min(p.ctx[s0 + i], p.ctx_cap) : 0;
+        const int nblk = (ctx[i] + kBlock - 1) / kBlock;
+        nbp[i] = (i < NS) ? min(nblk, b + p.pb) - b : 0;
+        npairs[i] = (nbp[i] + 1) >> 1;
+        nparts[i] = (nblk + p.pb - 1) / p.pb;
+        npmax = max(npmax, npairs[i]);
+    }
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 15;
+    const int q = lane >> 4;
+    const int owner = col / G;  // sequence of this column within its column set
+    int my_id[kMaxShareSeqs];
+#pragma unroll
+    for (int i = 0; i < kMaxShareSeqs; ++i) {
+        my_id[i] = (i < NS) ? load_ids(p.tables + (size_t)(s0 + i) * p.max_blocks, b, nbp[i], p.num_blocks) : 0;
+    }
+    // Each lane's Q^T operands wait in LDS (read back at every use) so the
+    // registers hold only the column states and one pair in flight.
+    // (They borrow the LDS of the wave states, which is free until the
+    // epilogue.)
+    static_assert(sizeof(u32x4) * CS * M::KSTEPS * kThreads <= sizeof(WaveState<D>), "Q operands exceed LDS");
+    u32x4(*qlds)[M::KSTEPS][kThreads] = reinterpret_cast<u32x4(*)[M::KSTEPS][kThreads]>(&st);
+    ColState<D> cst[CS];
+#pragma unroll
+    for (int c = 0; c < CS; ++c) {
+        u32x4 qr[M::KSTEPS];
+        load_qop<D, FMT>(p, s0 + c * TPG + owner, kvh * G + col % G, true, qr);
+#pragma unroll
+        for (int kk = 0; kk < M::KSTEPS; ++kk) qlds[c][kk][threadIdx.x] = qr[kk];
+        col_init(cst[c]);
+    }
+    auto qget = [&](int c, u32x4* qr) {
+#pragma unroll
+        for (int kk = 0; kk < M::KSTEPS; ++kk) qr[kk] = qlds[c][kk][threadIdx.x];
+    };
+
+    for (int k = wave; k < npmax; k += kWaves) {
+        const int t0 = (b + 2 * k) * kBlock;
+        const int a0 = readlane(my_id[0], 2 * k);
+        const int a1 = readlane(my_id[0], 2 * k + 1);
+        bool sh = true;
+#pragma unroll
+        for (int i = 0; i < kMaxShareSeqs; ++i) {
+            if (i < NS) {
+                sh = sh && t0 + 2 * kBlock <= ctx[i] && readlane(my_id[i], 2 * k) == a0 &&
+                     readlane(my_id[i], 2 * k + 1) == a1;
+            }
+        }
+        if (sh) {
+            // one load of the pair feeds every column set
+            KHalf<D, FMT> kr;
+            issue_k_pair<D, FMT, false>(p, kvh, a0, a1, kr);
+            f32x4 sc[CS][2];
+#pragma unroll
+            for (int c = 0; c < CS; ++c) {
+                u32x4 qr[M::KSTEPS];
+                qget(c, qr);
+                pair_scores<D, FMT>(kr, qr, sc[c][0], sc[c][1]);
+            }
+            // keep the V loads after the score MFMAs: K and V of the pair
+            // are never live together, which keeps the path in the
+            // per-sequence path's register budget
+            __builtin_amdgcn_sched_barrier(0);
+            VHalf<D, FMT> vr;
+            issue_v_pair<D, FMT, false>(p, kvh, a0, a1, vr);
+            const int full = t0 + 2 * kBlock;  // every token of the pair is in context
+#pragma unroll
+            for (int c = 0; c < CS; ++c) {
+                float x[8], pr[8];
+                scale_mask(sc[c][0], sc[c][1], p.scale_log2 * kr.s0, p.scale_log2 * kr.s1, t0 + 4 * q, full, true, x);
+                softmax_update(cst[c], x, pr);
+                pv_update<D, FMT>(cst[c], vr, pr, t0, full, true, true);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < CS; ++c) {
+                float x[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[i] = kNegInf;
+#pragma unroll
+                for (int i = 0; i < kMaxShareSeqs; ++i) {
+                    const int t = i - c * TPG;  // position of sequence i in this column set
+                    if (i < NS && t >= 0 && t < TPG && k < npairs[i]) {
+                        // one sequence's pair at a time (this path is rare:
+                        // register budget over latency)
+                        __builtin_amdgcn_sched_barrier(0);
+                        const bool has1 = 2 * k + 1 < nbp[i];
+                        const int n0 = readlane(my_id[i], 2 * k);
+                        const int n1 = has1 ? readlane(my_id[i], 2 * k + 1) : n0;
+                        KHalf<D, FMT> kr;
+                        issue_k_pair<D, FMT>(p, kvh, n0, n1, kr);
+                        f32x4 s0v, s1v;
+                        u32x4 qr[M::KSTEPS];
+                        qget(c, qr);
+                        pair_scores<D, FMT>(kr, qr, s0v, s1v);
+                        float xi[8];
+                        scale_mask(s0v, s1v, p.scale_log2 * kr.s0, p.scale_log2 * kr.s1, t0 + 4 * q, ctx[i], has1,
+                                   xi);
+                        if (owner == t) {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) x[e] = xi[e];
+                        }
+                    }
+                }
+                float pr[8];
+                softmax_update(cst[c], x, pr);
+#pragma unroll
+                for (int i = 0; i < kMaxShareSeqs; ++i) {
+                    const int t = i - c * TPG;
+                    if (i < NS && t >= 0 && t < TPG && k < npairs[i]) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        const bool has1 = 2 * k + 1 < nbp[i];
+                        const int n0 = readlane(my_id[i], 2 * k);
+                        const int n1 = has1 ? readlane(my_id[i], 2 * k + 1) : n0;
+                        VHalf<D, FMT> vr;
+                        issue_v_pair<D, FMT>(p, kvh, n0, n1, vr);
+                        pv_update<D, FMT>(cst[c], vr, pr, t0, ctx[i], has1, owner == t);
+                    }
+                }
+            }
+        }
+    }
+
+    // one column set at a time through the workgroup's LDS state
+#pragma unroll
+    for (int c = 0; c < CS; ++c) {
+        __syncthreads();  // the Q operands, or the previous set, have been read
+        col_to_lds(cst[c], st, wave);
+        __syncthreads();
+        merge_waves_store<D, F32OUT>(p, st, 16, part, [&](int cl, int& s, int& qh, int& np) {
+            const int i = c * TPG + cl / G;
+            s = s0 + i;
+            qh = kvh * G + cl % G;
+            np = nparts[0];
+#pragma unroll
+            for (int j = 1; j < kMaxShareSeqs; ++j) np = (i == j) ? nparts[j] : np;
+        });
+    }
+
+    __shared__ int last[kMaxShareSeqs];
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x < NS) {
+        const int i = threadIdx.x;
+        int np = nparts[0];
+#pragma unroll
+        for (int j = 1; j < kMaxShareSeqs; ++j) np = (i == j) ? nparts[j] : np;
+        last[i] = np > 1 && arrive(p, s0 + i, kvh, np);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kMaxShareSeqs; ++i) {
+        if (i < NS && last[i]) merge_partials<D, F32OUT>(p, s0 + i, kvh, nparts[i]);
+    }
 }
 
 }  // namespace pa

@@ -29,6 +29,8 @@ struct DecodeParams {
     int pmax;           // partitions per sequence at max_context_len
     int pb;             // blocks per partition (even)
     float scale_log2;   // log2(e) / sqrt(d)
+    int share_n;        // sequences per shared-prefix group (0: no shared-prefix workgroups)
+    int n_shared;       // shared-prefix workgroups, first in the grid: (S / share_n) * pmax * n_kv
 };
 
 // Bytes of the arrival-counter region at the start of a decode workspace:

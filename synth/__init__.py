@@ -12,6 +12,7 @@ from .gen import (  # noqa: F401
     f32_to_bf16_bits,
     make_decode_case,
     make_config_case,
+    make_clustered_prefix_case,
     make_mixed_case,
     make_prefill_case,
     make_probe_case,
@@ -19,6 +20,7 @@ from .gen import (  # noqa: F401
     permute_pool,
     poison_unused,
     private_twin,
+    privatize,
     used_slot_mask,
 )
 from .configs import CONFIGS, config_seed  # noqa: F401

@@ -457,3 +457,76 @@ def make_prefill_probe_case(n_heads, n_kv, d, dtype, ctx, q_lens, seed):
     if dtype == "bf16":
         q, k, v = f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
     return replace(base, dtype=dtype, q=q, k_slots=k, v_slots=v, name="prefill_probe")
+
+
+# ----------------------------------------------------------------------------
+# Prefix sharing in clusters
+# ----------------------------------------------------------------------------
+
+def make_clustered_prefix_case(n_heads, n_kv, d, dtype, clusters, seed, *, pool_factor=1.1, name="clusters"):
+    """Decode case whose sequences come in clusters, each cluster pointing the
+    first `prefix_blocks` entries of every member's table at the same
+    physical blocks (prefix caching at block granularity) and the rest at
+    private blocks. clusters: list of (prefix_blocks, [ctx of each member]).
+    A member may be shorter than its cluster's prefix: it then references
+    only the shared blocks it covers (its slots past ctx are never read)."""
+    kids = np.random.SeedSequence(seed).spawn(5)
+    ctx, plan = [], []
+    for pb_, members in clusters:
+        for c in members:
+            ctx.append(int(c))
+            plan.append(int(pb_))
+    ctx = np.asarray(ctx, dtype=np.int64)
+    need = 0
+    for pb_, members in clusters:
+        need += pb_
+        need += sum(max(0, _blocks(c) - pb_) for c in members)
+    pool_blocks = int(math.ceil(pool_factor * need))
+    perm = np.random.Generator(np.random.PCG64(kids[1])).permutation(pool_blocks).astype(np.int32)
+    mb = max(1, max(_blocks(c) for c in ctx))
+    tables = np.full((len(ctx), mb), -1, dtype=np.int32)
+    cursor, s = 0, 0
+    for pb_, members in clusters:
+        shared = perm[cursor:cursor + pb_]
+        cursor += pb_
+        for c in members:
+            nb = _blocks(c)
+            k = min(nb, pb_)
+            tables[s, :k] = shared[:k]
+            priv = max(0, nb - pb_)
+            tables[s, k:k + priv] = perm[cursor:cursor + priv]
+            cursor += priv
+            s += 1
+    assert cursor == need
+    S = len(ctx)
+    q = _normal(kids[2], S * n_heads * d, dtype).reshape(S, n_heads, d)
+    k = _normal(kids[3], pool_blocks * BLOCK_SIZE * n_kv * d, dtype).reshape(pool_blocks * BLOCK_SIZE, n_kv, d)
+    v = _normal(kids[4], pool_blocks * BLOCK_SIZE * n_kv * d, dtype).reshape(pool_blocks * BLOCK_SIZE, n_kv, d)
+    return DecodeCase(n_heads, n_kv, d, dtype, q, k, v, tables, ctx.astype(np.int32), pool_blocks, name=name,
+                      seed=int(seed))
+
+
+def privatize(case: DecodeCase) -> DecodeCase:
+    """Same sequences with no physical block referenced twice: every
+    (sequence, logical block) gets its own copy of the block it pointed at,
+    appended after the original pool."""
+    S, bs = case.num_seqs, BLOCK_SIZE
+    nblk = [_blocks(c) for c in case.context_lens]
+    NB = case.num_blocks
+    NB2 = NB + sum(nblk)
+    shp = case.k_slots.shape[1:]
+    k = np.empty((NB2 * bs,) + shp, dtype=case.k_slots.dtype)
+    v = np.empty_like(k)
+    k[:NB * bs] = case.k_slots
+    v[:NB * bs] = case.v_slots
+    tables = case.block_tables.copy()
+    dst = NB
+    for s in range(S):
+        for j in range(nblk[s]):
+            src = int(case.block_tables[s, j])
+            k[dst * bs:(dst + 1) * bs] = case.k_slots[src * bs:(src + 1) * bs]
+            v[dst * bs:(dst + 1) * bs] = case.v_slots[src * bs:(src + 1) * bs]
+            tables[s, j] = dst
+            dst += 1
+    return replace(case, k_slots=k, v_slots=v, block_tables=tables, num_blocks=NB2, shared_prefix_blocks=0,
+                   name=case.name + "/private")

@@ -4,8 +4,9 @@ import pytest
 import torch
 
 import oracle
-from synth import (make_config_case, make_decode_case, make_mixed_case, make_probe_case, permute_pool,
-                   poison_unused, private_twin)
+from synth.gen import bf16_bits_to_f32
+from synth import (make_clustered_prefix_case, make_config_case, make_decode_case, make_mixed_case, make_probe_case,
+                   permute_pool, poison_unused, private_twin, privatize)
 from tests.gpu_util import assert_close, dev_to_f64, gpu_decode, np_to_dev, oracle_decode, upload_meta, upload_pools
 
 pytestmark = pytest.mark.gpu
@@ -78,6 +79,50 @@ def test_shared_equals_private_bitexact(lib):
     b = gpu_decode(t).cpu()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert_close(dev_to_f64(a), oracle_decode(c), "bf16", "shared")
+
+
+# Clusters of sequences sharing prefixes of several lengths: groups of
+# consecutive sequences that share the first pair of a partition go through
+# the shared-prefix workgroups, the rest through the per-sequence path. Some
+# clusters have odd sizes (groups straddle clusters), odd shared-block counts
+# (a shared run ends inside a pair), and members shorter than the prefix.
+CLUSTERS = [
+    (90, [1500, 1441, 1600, 1700, 1488, 1501]),
+    (57, [920, 1000, 912, 950, 930]),
+    (31, [600, 300, 497, 498]),
+    (12, [150, 190]),
+    (0, [700, 333, 64]),
+]
+
+
+@pytest.mark.parametrize("n_heads,n_kv", [(32, 4), (16, 4), (64, 8)])
+@pytest.mark.parametrize("pb", [0, 2, 4, 16, 64])
+def test_shared_prefix_clusters_bitexact(lib, n_heads, n_kv, pb):
+    """Shared blocks give bit-identical output to private copies of the same
+    data, whichever path computes each partition, and match the oracle."""
+    c = make_clustered_prefix_case(n_heads, n_kv, 128, "bf16", CLUSTERS, 310 + n_heads + pb)
+    t = privatize(c)
+    a = gpu_decode(c, partition_blocks=pb).cpu()
+    b = gpu_decode(t, partition_blocks=pb).cpu()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert_close(dev_to_f64(a), oracle_decode(c), "bf16", "clusters")
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_shared_prefix_quantized_bitexact(lib, bits):
+    from paged_kv_cache_429_amd import binding as B
+    outs = []
+    c = make_clustered_prefix_case(32, 4, 128, "bf16", CLUSTERS, 320 + bits)
+    for case in (c, privatize(c)):
+        kp, vp = upload_pools(case)
+        kc, ks = B.quantize(kp, bits=bits, kind=0, n_kv_heads=4, d_head=128)
+        vc, vs = B.quantize(vp, bits=bits, kind=1, n_kv_heads=4, d_head=128)
+        outs.append(gpu_decode(case, kp=kc, vp=vc, kv_bits=bits, k_scales=ks, v_scales=vs, partition_blocks=4).cpu())
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    rk, rks = oracle.quantize_tiles(bf16_bits_to_f32(c.k_slots), bits)
+    rv, rvs = oracle.quantize_tiles(bf16_bits_to_f32(c.v_slots), bits)
+    ref = oracle_decode(c, k_slots=oracle.dequantize(rk, rks), v_slots=oracle.dequantize(rv, rvs))
+    assert_close(dev_to_f64(outs[0]), ref, "bf16", f"clusters int{bits}")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -89,3 +89,36 @@ def test_permutation_is_bijection():
     assert np.array_equal(p.block_tables[m], pi[c.block_tables[m]])
     b = int(c.block_tables[0, 0])
     assert np.array_equal(p.k_slots[pi[b] * 16:(pi[b] + 1) * 16], c.k_slots[b * 16:(b + 1) * 16])
+
+
+def test_clustered_prefix_structure():
+    from synth import make_clustered_prefix_case
+    clusters = [(5, [100, 70, 33]), (2, [40, 16]), (0, [17])]
+    c = make_clustered_prefix_case(8, 2, 64, "f32", clusters, 11)
+    t = c.block_tables
+    # members of a cluster point their first min(nblk, P) entries at the same blocks
+    assert (t[0, :5] == t[1, :5]).all() and (t[2, :3] == t[0, :3]).all()
+    assert (t[3, :2] == t[4, :1].tolist() + [t[3, 1]]).all() and t[3, 0] == t[4, 0]
+    used = []
+    for s in range(c.num_seqs):
+        used += t[s, :-(-int(c.context_lens[s]) // 16)].tolist()
+    # every referenced block exists; only shared prefix blocks are referenced twice
+    assert min(used) >= 0 and max(used) < c.num_blocks
+    from collections import Counter
+    multi = {b for b, n in Counter(used).items() if n > 1}
+    assert multi == set(t[0, :5].tolist()) | {int(t[3, 0])}
+
+
+def test_privatize_references_each_block_once():
+    from synth import make_clustered_prefix_case, privatize
+    import oracle
+    c = make_clustered_prefix_case(8, 2, 64, "f32", [(4, [80, 64, 50]), (0, [9])], 12)
+    p = privatize(c)
+    used = []
+    for s in range(p.num_seqs):
+        used += p.block_tables[s, :-(-int(p.context_lens[s]) // 16)].tolist()
+    assert len(used) == len(set(used))
+    f = lambda x: oracle.as_f64(x, "f32")
+    a = oracle.paged_decode(f(c.q), f(c.k_slots), f(c.v_slots), c.block_tables, c.context_lens, n_kv=2)
+    b = oracle.paged_decode(f(p.q), f(p.k_slots), f(p.v_slots), p.block_tables, p.context_lens, n_kv=2)
+    assert np.array_equal(a, b)
