@@ -142,13 +142,20 @@ uint64_t pa_kv_cache_bytes(int n_layers, int n_kv_heads, int d_head, int kv_bits
  *              sequences and needs no initialisation. One workspace serves
  *              calls of any shape, but calls that share it must be ordered
  *              (same stream, or synchronised): overlapping calls race.
- * partition_blocks  blocks per context partition (even, 2..64), or 0 to let
- *              the library choose. Long contexts are split into partitions
- *              processed in parallel and merged by log-sum-exp within the
- *              same launch: the last partition of a (sequence, KV head) to
- *              finish merges them, in partition order. The split depends only on
- *              the arguments' values on the host and on each sequence's
- *              length, never on physical block ids.
+ * partition_blocks  blocks per context partition pb (even, 2..64), or 0 to
+ *              let the library choose. Long contexts are split into
+ *              partitions processed in parallel and merged by log-sum-exp
+ *              within the same launch: the last partition of a (sequence,
+ *              KV head) to finish merges them, in partition order. Partition
+ *              p starts at block p * pb; the last one also takes a remainder
+ *              of up to pb / 4 blocks. The split depends only on the
+ *              arguments' values on the host and on each sequence's length,
+ *              never on physical block ids.
+ *              Consecutive sequences (16 / G of them, for G = 4 or 8) whose
+ *              tables name the same physical blocks for a partition's first
+ *              two blocks are processed together, each shared block being
+ *              read once for the group; results are bit-identical to those
+ *              of private copies of the same blocks.
  * ------------------------------------------------------------------------ */
 size_t paged_attn_decode_workspace_size(int num_seqs, int n_heads, int n_kv_heads, int d_head,
                                         int max_context_len, int partition_blocks);

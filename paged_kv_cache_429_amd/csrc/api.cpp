@@ -98,7 +98,7 @@ size_t paged_attn_decode_workspace_size(int num_seqs, int n_heads, int n_kv_head
     if (num_seqs <= 0 || n_heads <= 0 || n_kv_heads <= 0 || d_head <= 0 || max_context_len <= 0) return 0;
     if (partition_blocks < 0 || partition_blocks > 64 || (partition_blocks & 1)) return 0;
     const int pb = plan_partition_blocks(num_seqs, n_kv_heads, max_context_len, partition_blocks);
-    const int pmax = ceil_div(ceil_div(max_context_len, PA_BLOCK_SIZE), pb);
+    const int pmax = pa::num_parts(ceil_div(max_context_len, PA_BLOCK_SIZE), pb);
     return pa::decode_workspace_bytes(num_seqs, n_heads, n_kv_heads, d_head, pmax);
 }
 
@@ -143,7 +143,7 @@ int paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
     p.group = G;
     // planned from max_context_len exactly as paged_attn_decode_workspace_size() does
     p.pb = plan_partition_blocks(num_seqs, n_kv_heads, std::max(1, max_context_len), partition_blocks);
-    p.pmax = ceil_div(ceil_div(p.ctx_cap, PA_BLOCK_SIZE), p.pb);
+    p.pmax = pa::num_parts(ceil_div(std::max(1, p.ctx_cap), PA_BLOCK_SIZE), p.pb);
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d_head));
 
     // Shared-prefix workgroups (groups of 16/G consecutive sequences whose

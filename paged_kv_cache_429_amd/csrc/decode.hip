@@ -51,7 +51,11 @@ void decode_kernel(DecodeParams p) {
     constexpr bool F32OUT = (FMT == FMT_F32);
     if constexpr (FMT != FMT_F32) {
         if ((int)blockIdx.x < p.n_shared) {
-            shared_unit<D, FMT, 1, F32OUT>(p, blockIdx.x, st);
+            if (p.share_n == 2) {
+                shared_unit<D, FMT, 1, 2, F32OUT>(p, blockIdx.x, st);
+            } else {
+                shared_unit<D, FMT, 1, 4, F32OUT>(p, blockIdx.x, st);
+            }
             return;
         }
     }
@@ -70,10 +74,10 @@ void decode_kernel(DecodeParams p) {
         return;
     }
     u.nblk = (u.ctx + kBlock - 1) / kBlock;
-    u.nparts = (u.nblk + p.pb - 1) / p.pb;
+    u.nparts = num_parts(u.nblk, p.pb);
     if (u.part >= u.nparts) return;
     u.b_begin = u.part * p.pb;
-    u.b_end = min(u.nblk, u.b_begin + p.pb);
+    u.b_end = part_end(u.nblk, p.pb, u.part, u.nparts);
     if (p.share_n > 0) {  // taken by a shared-prefix workgroup?
         const int grp = u.s / p.share_n;
         if ((grp + 1) * p.share_n <= p.num_seqs && group_shares(p, grp * p.share_n, u.part)) return;
@@ -87,8 +91,10 @@ void decode_kernel(DecodeParams p) {
         __syncthreads();
         f32_wave<D>(p, u, trow, st, qs);
     } else {
-        const int my_id = load_ids(trow, u.b_begin, u.b_end - u.b_begin, p.num_blocks);
-        mfma_wave<D, FMT>(p, u, my_id, st);
+        const int nbp = u.b_end - u.b_begin;
+        const int id_lo = load_ids(trow, u.b_begin, min(nbp, 64), p.num_blocks);
+        const int id_hi = nbp > 64 ? load_ids(trow, u.b_begin + 64, nbp - 64, p.num_blocks) : 0;
+        mfma_wave<D, FMT>(p, u, id_lo, id_hi, st);
     }
     epilogue<D, F32OUT>(p, u, st);
 }

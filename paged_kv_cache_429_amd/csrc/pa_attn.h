@@ -30,8 +30,12 @@ struct Unit {
     int s, kvh, part, ctx, nblk, nparts, b_begin, b_end;
 };
 
-__device__ __forceinline__ int tile_id(const DecodeParams& p, int my_id, int j) {
-    return readlane(my_id, j);
+// Physical id of block j (wave-uniform, 0 <= j < 128) of a partition whose
+// ids are spread over two lane registers (blocks 0..63 and 64..127).
+__device__ __forceinline__ int tile_id(int id_lo, int id_hi, int j) {
+    const int a = readlane(id_lo, j & 63);
+    const int b = readlane(id_hi, j & 63);
+    return j < 64 ? a : b;
 }
 
 // -----------------------------------------------------------------------------
@@ -337,16 +341,66 @@ __device__ __forceinline__ void load_qop(const DecodeParams& p, int s, int qh, b
     }
 }
 
+// Software-pipelined run of pairs k, k + 4, ... of one wave (pair k must
+// exist; the run continues while more(next) holds). K of the next pair loads
+// during this pair's softmax and P.V, V of the next pair during its Q.K; the
+// last pair of the run is peeled off so that every load in the loop is
+// unconditional and the wait before each use covers only the half it reads.
+//   ids(k, i0, i1)          physical ids of the pair's blocks
+//   geo(k, t0, ctx, has1)   first token, the context that masks it, and
+//                           whether its second block exists
+// NT selects the streaming load policy; lanes with own == false (columns of
+// another sequence) see -inf scores and a zero P column, which leave their
+// state unchanged. Returns the first pair after the run.
+template <int D, int FMT, bool NT, typename Ids, typename More, typename Geo>
+__device__ __forceinline__ int pair_run(const DecodeParams& p, int kvh, const u32x4* qop, ColState<D>& cs, int k,
+                                        Ids ids, More more, Geo geo, bool own = true) {
+    const int q = (threadIdx.x & 63) >> 4;
+    KHalf<D, FMT> kr;
+    VHalf<D, FMT> vr;
+    auto step = [&](int kk, bool prefetch) {
+        int t0, ctx;
+        bool has1;
+        geo(kk, t0, ctx, has1);
+        f32x4 s0, s1;
+        pair_scores<D, FMT>(kr, qop, s0, s1);
+        // take the K scales before the prefetch replaces them
+        const float c0 = p.scale_log2 * kr.s0;
+        const float c1 = p.scale_log2 * kr.s1;
+        int n0 = 0, n1 = 0;
+        if (prefetch) {
+            ids(kk + kWaves, n0, n1);
+            issue_k_pair<D, FMT, NT>(p, kvh, n0, n1, kr);
+        }
+        float x[8], pr[8];
+        scale_mask(s0, s1, c0, c1, t0 + 4 * q, ctx, has1, x);
+        if (!own) {  // a column of another sequence: no update
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = kNegInf;
+        }
+        softmax_update(cs, x, pr);
+        pv_update<D, FMT>(cs, vr, pr, t0, ctx, has1, own);
+        if (prefetch) issue_v_pair<D, FMT, NT>(p, kvh, n0, n1, vr);
+    };
+    int i0, i1;
+    ids(k, i0, i1);
+    issue_k_pair<D, FMT, NT>(p, kvh, i0, i1, kr);
+    issue_v_pair<D, FMT, NT>(p, kvh, i0, i1, vr);
+    for (; more(k + kWaves); k += kWaves) step(k, true);
+    step(k, false);
+    return k + kWaves;
+}
+
 // One wave of a (sequence, KV head, partition) workgroup: pairs wave,
 // wave + 4, ... of the partition, the G query heads of the KV head in
 // columns 0..G-1.
 template <int D, int FMT>
-__device__ __forceinline__ void mfma_wave(const DecodeParams& p, const Unit& u, int my_id, WaveState<D>& st) {
+__device__ __forceinline__ void mfma_wave(const DecodeParams& p, const Unit& u, int id_lo, int id_hi,
+                                          WaveState<D>& st) {
     using M = Mfma<D, FMT>;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane & 15;
-    const int q = lane >> 4;
 
     u32x4 qop[M::KSTEPS];
     load_qop<D, FMT>(p, u.s, u.kvh * p.group + g, g < p.group, qop);
@@ -355,46 +409,20 @@ __device__ __forceinline__ void mfma_wave(const DecodeParams& p, const Unit& u, 
 
     const int nb_part = u.b_end - u.b_begin;
     const int npairs = (nb_part + 1) >> 1;
-    // physical ids of the two blocks of pair k (a missing second block
-    // repeats the first, which is then masked out)
-    auto ids = [&](int k, int& i0, int& i1) {
-        i0 = tile_id(p, my_id, 2 * k);
-        i1 = (2 * k + 1) < nb_part ? tile_id(p, my_id, 2 * k + 1) : i0;
-    };
-    auto step = [&](int k, const KHalf<D, FMT>& kr, const VHalf<D, FMT>& vr, bool prefetch, KHalf<D, FMT>& kn,
-                    VHalf<D, FMT>& vn) {
-        const int t0 = (u.b_begin + 2 * k) * kBlock;
-        const bool has1 = 2 * k + 1 < nb_part;
-        f32x4 s0, s1;
-        pair_scores<D, FMT>(kr, qop, s0, s1);
-        // (kn may be kr: take the K scales before the prefetch replaces them)
-        const float c0 = p.scale_log2 * kr.s0;
-        const float c1 = p.scale_log2 * kr.s1;
-        int n0 = 0, n1 = 0;
-        if (prefetch) {
-            ids(k + kWaves, n0, n1);
-            issue_k_pair<D, FMT>(p, u.kvh, n0, n1, kn);
-        }
-        float x[8], pr[8];
-        scale_mask(s0, s1, c0, c1, t0 + 4 * q, u.ctx, has1, x);
-        softmax_update(cs, x, pr);
-        pv_update<D, FMT>(cs, vr, pr, t0, u.ctx, has1, true);
-        if (prefetch) issue_v_pair<D, FMT>(p, u.kvh, n0, n1, vn);
-    };
-
-    // Waves take pairs wave, wave+4, ... In the steady loop the next pair
-    // always exists, so every load is unconditional and the wait before each
-    // use covers only the half it reads; the last pair runs after the loop.
-    int k = wave;
-    if (k < npairs) {
-        KHalf<D, FMT> kr;
-        VHalf<D, FMT> vr;
-        int i0, i1;
-        ids(k, i0, i1);
-        issue_k_pair<D, FMT>(p, u.kvh, i0, i1, kr);
-        issue_v_pair<D, FMT>(p, u.kvh, i0, i1, vr);
-        for (; k + kWaves < npairs; k += kWaves) step(k, kr, vr, true, kr, vr);
-        step(k, kr, vr, false, kr, vr);
+    if (wave < npairs) {
+        pair_run<D, FMT, true>(
+            p, u.kvh, qop, cs, wave,
+            // a missing second block repeats the first, which is then masked out
+            [&](int k, int& i0, int& i1) {
+                i0 = tile_id(id_lo, id_hi, 2 * k);
+                i1 = (2 * k + 1) < nb_part ? tile_id(id_lo, id_hi, 2 * k + 1) : i0;
+            },
+            [&](int k) { return k < npairs; },
+            [&](int k, int& t0, int& ctx, bool& has1) {
+                t0 = (u.b_begin + 2 * k) * kBlock;
+                ctx = u.ctx;
+                has1 = 2 * k + 1 < nb_part;
+            });
     }
     col_to_lds(cs, st, wave);
 }
@@ -445,7 +473,7 @@ __device__ __forceinline__ void f32_wave(const DecodeParams& p, const Unit& u, c
             window = j >> 6;
             my_id = load_ids(trow, u.b_begin + (window << 6), min(64, nb_part - (window << 6)), p.num_blocks);
         }
-        const int id = tile_id(p, my_id, j & 63);
+        const int id = readlane(my_id, j & 63);
         const size_t toff = ((size_t)id * p.n_kv + u.kvh) * TILE;
         const float* kt = reinterpret_cast<const float*>(kbase + toff);
         const float* vt = reinterpret_cast<const float*>(vbase + toff);
@@ -692,48 +720,57 @@ __device__ __forceinline__ void epilogue(const DecodeParams& p, const Unit& u, W
 // which kind of workgroup computed it: shared blocks give bit-identical
 // output to private copies of the same data.
 // -----------------------------------------------------------------------------
-constexpr int kMaxShareSeqs = 4;
+constexpr int kMaxShareSeqs = 4;  // sequences of a group (16 / G for G = 4 or 8)
 
 // Do the share_n sequences from s0 on all hold the first block pair of
-// partition `part`, full, at the same physical ids?
+// partition `part`, full, at the same physical ids? Every length and table
+// entry is fetched unconditionally (indices clamped into the arrays), so the
+// test costs one round of loads rather than a chain of dependent ones.
 __device__ __forceinline__ bool group_shares(const DecodeParams& p, int s0, int part) {
     const int b = part * p.pb;
     const int need = (b + 2) * kBlock;
-    for (int i = 0; i < p.share_n; ++i) {
-        if (min(p.ctx[s0 + i], p.ctx_cap) < need) return false;
+    const int b1 = min(b + 1, p.max_blocks - 1);  // b < max_blocks always
+    int ctx[kMaxShareSeqs], e0[kMaxShareSeqs], e1[kMaxShareSeqs];
+#pragma unroll
+    for (int i = 0; i < kMaxShareSeqs; ++i) {
+        const int s = s0 + min(i, p.share_n - 1);
+        ctx[i] = p.ctx[s];
+        const int32_t* t = p.tables + (size_t)s * p.max_blocks;
+        e0[i] = t[b];
+        e1[i] = t[b1];
     }
-    const int32_t* t0 = p.tables + (size_t)s0 * p.max_blocks + b;
-    const int id0 = t0[0], id1 = t0[1];
-    for (int i = 1; i < p.share_n; ++i) {
-        const int32_t* ti = p.tables + (size_t)(s0 + i) * p.max_blocks + b;
-        if (ti[0] != id0 || ti[1] != id1) return false;
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < kMaxShareSeqs; ++i) {
+        const int c = min(ctx[i], p.ctx_cap);
+        ok = ok && c >= need && num_parts((c + kBlock - 1) / kBlock, p.pb) > part && e0[i] == e0[0] &&
+             e1[i] == e1[0];
     }
-    return true;
+    return ok;
 }
 
-template <int D, int FMT, int CS, bool F32OUT>
+template <int D, int FMT, int CS, int NS, bool F32OUT>
 __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, WaveState<D>& st) {
     using M = Mfma<D, FMT>;
     const int kvh = unit % p.n_kv;
     const int rest = unit / p.n_kv;
     const int part = rest % p.pmax;
     const int grp = rest / p.pmax;
-    const int NS = p.share_n;
     const int s0 = grp * NS;
     if (!group_shares(p, s0, part)) return;
 
     const int G = p.group;
     const int TPG = 16 / G;  // sequences per column set
     const int b = part * p.pb;
-    int ctx[kMaxShareSeqs], nbp[kMaxShareSeqs], npairs[kMaxShareSeqs], nparts[kMaxShareSeqs];
+    int ctx[NS], nbp[NS], npairs[NS], nparts[NS];
     int npmax = 0;
 #pragma unroll
-    for (int i = 0; i < kMaxShareSeqs; ++i) {
-        ctx[i] = (i < NS) ? min(p.ctx[s0 + i], p.ctx_cap) : 0;
+    for (int i = 0; i < NS; ++i) {
+        ctx[i] = min(p.ctx[s0 + i], p.ctx_cap);
         const int nblk = (ctx[i] + kBlock - 1) / kBlock;
-        nbp[i] = (i < NS) ? min(nblk, b + p.pb) - b : 0;
+        nparts[i] = num_parts(nblk, p.pb);
+        nbp[i] = part_end(nblk, p.pb, part, nparts[i]) - b;
         npairs[i] = (nbp[i] + 1) >> 1;
-        nparts[i] = (nblk + p.pb - 1) / p.pb;
         npmax = max(npmax, npairs[i]);
     }
 
@@ -742,112 +779,157 @@ __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, Wav
     const int col = lane & 15;
     const int q = lane >> 4;
     const int owner = col / G;  // sequence of this column within its column set
-    int my_id[kMaxShareSeqs];
+    int my_id[NS], my_hi[NS];
 #pragma unroll
-    for (int i = 0; i < kMaxShareSeqs; ++i) {
-        my_id[i] = (i < NS) ? load_ids(p.tables + (size_t)(s0 + i) * p.max_blocks, b, nbp[i], p.num_blocks) : 0;
+    for (int i = 0; i < NS; ++i) {
+        const int32_t* trow = p.tables + (size_t)(s0 + i) * p.max_blocks;
+        my_id[i] = load_ids(trow, b, min(nbp[i], 64), p.num_blocks);
+        my_hi[i] = nbp[i] > 64 ? load_ids(trow, b + 64, nbp[i] - 64, p.num_blocks) : 0;
     }
-    // Each lane's Q^T operands wait in LDS (read back at every use) so the
-    // registers hold only the column states and one pair in flight.
-    // (They borrow the LDS of the wave states, which is free until the
-    // epilogue.)
-    static_assert(sizeof(u32x4) * CS * M::KSTEPS * kThreads <= sizeof(WaveState<D>), "Q operands exceed LDS");
-    u32x4(*qlds)[M::KSTEPS][kThreads] = reinterpret_cast<u32x4(*)[M::KSTEPS][kThreads]>(&st);
+
+    u32x4 qop[CS][M::KSTEPS];
     ColState<D> cst[CS];
 #pragma unroll
     for (int c = 0; c < CS; ++c) {
-        u32x4 qr[M::KSTEPS];
-        load_qop<D, FMT>(p, s0 + c * TPG + owner, kvh * G + col % G, true, qr);
-#pragma unroll
-        for (int kk = 0; kk < M::KSTEPS; ++kk) qlds[c][kk][threadIdx.x] = qr[kk];
+        load_qop<D, FMT>(p, s0 + c * TPG + owner, kvh * G + col % G, true, qop[c]);
         col_init(cst[c]);
     }
     auto qget = [&](int c, u32x4* qr) {
 #pragma unroll
-        for (int kk = 0; kk < M::KSTEPS; ++kk) qr[kk] = qlds[c][kk][threadIdx.x];
+        for (int kk = 0; kk < M::KSTEPS; ++kk) qr[kk] = qop[c][kk];
     };
-
-    for (int k = wave; k < npmax; k += kWaves) {
+    // Pair k is shared when every sequence of the group holds both its
+    // blocks, full, at the same physical ids.
+    auto shared_pair = [&](int k) {
         const int t0 = (b + 2 * k) * kBlock;
-        const int a0 = readlane(my_id[0], 2 * k);
-        const int a1 = readlane(my_id[0], 2 * k + 1);
+        const int a0 = tile_id(my_id[0], my_hi[0], 2 * k);
+        const int a1 = tile_id(my_id[0], my_hi[0], 2 * k + 1);
         bool sh = true;
 #pragma unroll
-        for (int i = 0; i < kMaxShareSeqs; ++i) {
+        for (int i = 0; i < NS; ++i) {
             if (i < NS) {
-                sh = sh && t0 + 2 * kBlock <= ctx[i] && readlane(my_id[i], 2 * k) == a0 &&
-                     readlane(my_id[i], 2 * k + 1) == a1;
+                sh = sh && t0 + 2 * kBlock <= ctx[i] && tile_id(my_id[i], my_hi[i], 2 * k) == a0 &&
+                     tile_id(my_id[i], my_hi[i], 2 * k + 1) == a1;
             }
         }
-        if (sh) {
-            // one load of the pair feeds every column set
-            KHalf<D, FMT> kr;
-            issue_k_pair<D, FMT, false>(p, kvh, a0, a1, kr);
-            f32x4 sc[CS][2];
+        return sh;
+    };
+
+    int k = wave;
+    if (CS == 1 && k < npmax && shared_pair(k)) {
+        // the leading run of shared pairs, pipelined like the per-sequence
+        // path and with the same per-column operations (every token of a
+        // shared pair is in context)
+        k = pair_run<D, FMT, false>(
+            p, kvh, qop[0], cst[0], k,
+            [&](int kk, int& i0, int& i1) {
+                i0 = tile_id(my_id[0], my_hi[0], 2 * kk);
+                i1 = tile_id(my_id[0], my_hi[0], 2 * kk + 1);
+            },
+            [&](int kk) { return kk < npmax && shared_pair(kk); },
+            [&](int kk, int& t0, int& cx, bool& has1) {
+                t0 = (b + 2 * kk) * kBlock;
+                cx = t0 + 2 * kBlock;
+                has1 = true;
+            });
+    }
+    if (CS == 1) {
+        // The rest, sequence by sequence: each sequence's remaining pairs
+        // (in order) as one pipelined run that updates only its columns.
 #pragma unroll
-            for (int c = 0; c < CS; ++c) {
-                u32x4 qr[M::KSTEPS];
-                qget(c, qr);
-                pair_scores<D, FMT>(kr, qr, sc[c][0], sc[c][1]);
+        for (int i = 0; i < NS; ++i) {
+            if (k < npairs[i]) {
+                pair_run<D, FMT, true>(
+                    p, kvh, qop[0], cst[0], k,
+                    [&](int kk, int& i0, int& i1) {
+                        i0 = tile_id(my_id[i], my_hi[i], 2 * kk);
+                        i1 = (2 * kk + 1) < nbp[i] ? tile_id(my_id[i], my_hi[i], 2 * kk + 1) : i0;
+                    },
+                    [&](int kk) { return kk < npairs[i]; },
+                    [&](int kk, int& t0, int& cx, bool& has1) {
+                        t0 = (b + 2 * kk) * kBlock;
+                        cx = ctx[i];
+                        has1 = 2 * kk + 1 < nbp[i];
+                    },
+                    owner == i);
             }
-            // keep the V loads after the score MFMAs: K and V of the pair
-            // are never live together, which keeps the path in the
-            // per-sequence path's register budget
-            __builtin_amdgcn_sched_barrier(0);
-            VHalf<D, FMT> vr;
-            issue_v_pair<D, FMT, false>(p, kvh, a0, a1, vr);
-            const int full = t0 + 2 * kBlock;  // every token of the pair is in context
-#pragma unroll
-            for (int c = 0; c < CS; ++c) {
-                float x[8], pr[8];
-                scale_mask(sc[c][0], sc[c][1], p.scale_log2 * kr.s0, p.scale_log2 * kr.s1, t0 + 4 * q, full, true, x);
-                softmax_update(cst[c], x, pr);
-                pv_update<D, FMT>(cst[c], vr, pr, t0, full, true, true);
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < CS; ++c) {
-                float x[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) x[i] = kNegInf;
-#pragma unroll
-                for (int i = 0; i < kMaxShareSeqs; ++i) {
-                    const int t = i - c * TPG;  // position of sequence i in this column set
-                    if (i < NS && t >= 0 && t < TPG && k < npairs[i]) {
-                        // one sequence's pair at a time (this path is rare:
-                        // register budget over latency)
-                        __builtin_amdgcn_sched_barrier(0);
-                        const bool has1 = 2 * k + 1 < nbp[i];
-                        const int n0 = readlane(my_id[i], 2 * k);
-                        const int n1 = has1 ? readlane(my_id[i], 2 * k + 1) : n0;
-                        KHalf<D, FMT> kr;
-                        issue_k_pair<D, FMT>(p, kvh, n0, n1, kr);
-                        f32x4 s0v, s1v;
-                        u32x4 qr[M::KSTEPS];
-                        qget(c, qr);
-                        pair_scores<D, FMT>(kr, qr, s0v, s1v);
-                        float xi[8];
-                        scale_mask(s0v, s1v, p.scale_log2 * kr.s0, p.scale_log2 * kr.s1, t0 + 4 * q, ctx[i], has1,
-                                   xi);
-                        if (owner == t) {
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) x[e] = xi[e];
+        }
+    } else {
+        // the rest, one pair at a time (shared or not)
+        for (; k < npmax; k += kWaves) {
+            const int t0 = (b + 2 * k) * kBlock;
+            const int a0 = tile_id(my_id[0], my_hi[0], 2 * k);
+            const int a1 = tile_id(my_id[0], my_hi[0], 2 * k + 1);
+            if (shared_pair(k)) {
+                // one load of the pair feeds every column set
+                KHalf<D, FMT> kr;
+                issue_k_pair<D, FMT, false>(p, kvh, a0, a1, kr);
+                f32x4 sc[CS][2];
+    #pragma unroll
+                for (int c = 0; c < CS; ++c) {
+                    u32x4 qr[M::KSTEPS];
+                    qget(c, qr);
+                    pair_scores<D, FMT>(kr, qr, sc[c][0], sc[c][1]);
+                }
+                // keep the V loads after the score MFMAs: K and V of the pair
+                // are never live together, which keeps the path in the
+                // per-sequence path's register budget
+                __builtin_amdgcn_sched_barrier(0);
+                VHalf<D, FMT> vr;
+                issue_v_pair<D, FMT, false>(p, kvh, a0, a1, vr);
+                const int full = t0 + 2 * kBlock;  // every token of the pair is in context
+    #pragma unroll
+                for (int c = 0; c < CS; ++c) {
+                    float x[8], pr[8];
+                    scale_mask(sc[c][0], sc[c][1], p.scale_log2 * kr.s0, p.scale_log2 * kr.s1, t0 + 4 * q, full, true, x);
+                    softmax_update(cst[c], x, pr);
+                    pv_update<D, FMT>(cst[c], vr, pr, t0, full, true, true);
+                }
+            } else {
+    #pragma unroll
+                for (int c = 0; c < CS; ++c) {
+                    float x[8];
+    #pragma unroll
+                    for (int i = 0; i < 8; ++i) x[i] = kNegInf;
+    #pragma unroll
+                    for (int i = 0; i < NS; ++i) {
+                        const int t = i - c * TPG;  // position of sequence i in this column set
+                        if (i < NS && t >= 0 && t < TPG && k < npairs[i]) {
+                            // one sequence's pair at a time (this path is rare:
+                            // register budget over latency)
+                            __builtin_amdgcn_sched_barrier(0);
+                            const bool has1 = 2 * k + 1 < nbp[i];
+                            const int n0 = tile_id(my_id[i], my_hi[i], 2 * k);
+                            const int n1 = has1 ? tile_id(my_id[i], my_hi[i], 2 * k + 1) : n0;
+                            KHalf<D, FMT> kr;
+                            issue_k_pair<D, FMT>(p, kvh, n0, n1, kr);
+                            f32x4 s0v, s1v;
+                            u32x4 qr[M::KSTEPS];
+                            qget(c, qr);
+                            pair_scores<D, FMT>(kr, qr, s0v, s1v);
+                            float xi[8];
+                            scale_mask(s0v, s1v, p.scale_log2 * kr.s0, p.scale_log2 * kr.s1, t0 + 4 * q, ctx[i], has1,
+                                       xi);
+                            if (owner == t) {
+    #pragma unroll
+                                for (int e = 0; e < 8; ++e) x[e] = xi[e];
+                            }
                         }
                     }
-                }
-                float pr[8];
-                softmax_update(cst[c], x, pr);
-#pragma unroll
-                for (int i = 0; i < kMaxShareSeqs; ++i) {
-                    const int t = i - c * TPG;
-                    if (i < NS && t >= 0 && t < TPG && k < npairs[i]) {
-                        __builtin_amdgcn_sched_barrier(0);
-                        const bool has1 = 2 * k + 1 < nbp[i];
-                        const int n0 = readlane(my_id[i], 2 * k);
-                        const int n1 = has1 ? readlane(my_id[i], 2 * k + 1) : n0;
-                        VHalf<D, FMT> vr;
-                        issue_v_pair<D, FMT>(p, kvh, n0, n1, vr);
-                        pv_update<D, FMT>(cst[c], vr, pr, t0, ctx[i], has1, owner == t);
+                    float pr[8];
+                    softmax_update(cst[c], x, pr);
+    #pragma unroll
+                    for (int i = 0; i < NS; ++i) {
+                        const int t = i - c * TPG;
+                        if (i < NS && t >= 0 && t < TPG && k < npairs[i]) {
+                            __builtin_amdgcn_sched_barrier(0);
+                            const bool has1 = 2 * k + 1 < nbp[i];
+                            const int n0 = tile_id(my_id[i], my_hi[i], 2 * k);
+                            const int n1 = has1 ? tile_id(my_id[i], my_hi[i], 2 * k + 1) : n0;
+                            VHalf<D, FMT> vr;
+                            issue_v_pair<D, FMT>(p, kvh, n0, n1, vr);
+                            pv_update<D, FMT>(cst[c], vr, pr, t0, ctx[i], has1, owner == t);
+                        }
                     }
                 }
             }
@@ -857,7 +939,7 @@ __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, Wav
     // one column set at a time through the workgroup's LDS state
 #pragma unroll
     for (int c = 0; c < CS; ++c) {
-        __syncthreads();  // the Q operands, or the previous set, have been read
+        __syncthreads();  // every wave is done with the previous set
         col_to_lds(cst[c], st, wave);
         __syncthreads();
         merge_waves_store<D, F32OUT>(p, st, 16, part, [&](int cl, int& s, int& qh, int& np) {
@@ -866,23 +948,23 @@ __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, Wav
             qh = kvh * G + cl % G;
             np = nparts[0];
 #pragma unroll
-            for (int j = 1; j < kMaxShareSeqs; ++j) np = (i == j) ? nparts[j] : np;
+            for (int j = 1; j < NS; ++j) np = (i == j) ? nparts[j] : np;
         });
     }
 
-    __shared__ int last[kMaxShareSeqs];
+    __shared__ int last[NS];
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x < NS) {
         const int i = threadIdx.x;
         int np = nparts[0];
 #pragma unroll
-        for (int j = 1; j < kMaxShareSeqs; ++j) np = (i == j) ? nparts[j] : np;
+        for (int j = 1; j < NS; ++j) np = (i == j) ? nparts[j] : np;
         last[i] = np > 1 && arrive(p, s0 + i, kvh, np);
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kMaxShareSeqs; ++i) {
+    for (int i = 0; i < NS; ++i) {
         if (i < NS && last[i]) merge_partials<D, F32OUT>(p, s0 + i, kvh, nparts[i]);
     }
 }

@@ -7,6 +7,25 @@
 
 namespace pa {
 
+// Context partitions of a sequence of nblk blocks (nblk >= 1) at pb blocks
+// per partition. Partition p starts at block p * pb and holds pb blocks; the
+// last one runs to the end of the sequence and absorbs a remainder of at
+// most pb / 4 blocks instead of leaving it as a short partition of its own
+// (a short partition's workgroup never fills its load pipeline). Partitions
+// therefore hold up to 5 pb / 4 blocks. Depends only on the length, never on
+// block ids.
+constexpr int kAbsorbDiv = 4;
+__host__ __device__ inline int num_parts(int nblk, int pb) {
+    const int full = nblk / pb;
+    const int rem = nblk - full * pb;
+    const int thr = pb / kAbsorbDiv;
+    const int n = full + (rem > thr ? 1 : 0);
+    return n > 1 ? n : 1;
+}
+__host__ __device__ inline int part_end(int nblk, int pb, int part, int nparts) {
+    return part + 1 == nparts ? nblk : (part + 1) * pb;
+}
+
 struct DecodeParams {
     const void* q;
     const void* k_pool;
@@ -26,7 +45,7 @@ struct DecodeParams {
     int n_heads;
     int n_kv;
     int group;
-    int pmax;           // partitions per sequence at max_context_len
+    int pmax;           // num_parts() of a sequence at max_context_len
     int pb;             // blocks per partition (even)
     float scale_log2;   // log2(e) / sqrt(d)
     int share_n;        // sequences per shared-prefix group (0: no shared-prefix workgroups)

@@ -59,6 +59,18 @@ def test_partition_invariance(lib, pb):
     _parity(c, partition_blocks=pb)
 
 
+@pytest.mark.parametrize("pb", [2, 16, 64])
+def test_partition_rounding_boundaries(lib, pb):
+    """Partitions hold pb blocks, the last one absorbing a remainder of up
+    to pb / 4 blocks (so beyond 64 blocks at pb = 64): lengths around every
+    boundary of that rule."""
+    r = max(1, pb // 4)
+    nb = [pb - 1, pb, pb + 1, pb + r - 1, pb + r, pb + r + 1, 2 * pb, 2 * pb + r, 2 * pb + r + 1, 3 * pb - 1]
+    ctx = sorted({max(1, 16 * n - 3) for n in nb} | {max(1, 16 * n) for n in nb})
+    c = make_decode_case(16, 4, 128, "bf16", ctx, 330 + pb, pool_factor=1.2)
+    _parity(c, partition_blocks=pb)
+
+
 def test_long_context_many_partitions(lib):
     c = make_decode_case(32, 8, 128, "bf16", [16384, 9000, 1, 12345], 301, pool_factor=1.05)
     _parity(c)
