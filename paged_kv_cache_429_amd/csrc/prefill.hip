@@ -20,6 +20,8 @@
 //
 // fp32 KV: each (chunk row, KV head) runs the decode VALU loop with the
 // row's causal context.
+#include <type_traits>
+
 #include "pa_attn.h"
 
 namespace pa {
@@ -252,6 +254,272 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p, int 
     }
 }
 
+// -----------------------------------------------------------------------------
+// Tile path (bf16 KV, d_head 128, G dividing 32). One workgroup of 8 waves
+// per (sequence, KV head, tile of 256/G chunk tokens); wave w owns 32 query
+// rows (32/G tokens x G heads), one 32-column MFMA tile, so every MFMA is
+// 32x32x16 with all columns in use, and two waves share each SIMD (one
+// wave's softmax overlaps the other's MFMAs). Keys stream through LDS in
+// stages of 64 (four blocks of K, then four of V, 32 KiB), double-buffered:
+// the next stage's loads are in flight while this stage is computed, and
+// one barrier per stage hands the buffer over. Per stage and wave:
+//   S^T[64 keys x 32 rows] = K Q^T      (16 MFMA, K rows read from LDS)
+//   online softmax per row (column), causal mask by select on the diagonal
+//   O^T[128 x 32 rows]     += V^T P^T   (16 MFMA, V^T read from LDS)
+// The S^T accumulator of a lane is exactly its P^T operand (keys
+// 8*(r/4) + 4*(l/32) + r%4 of its column), and the V^T operand reads the
+// same keys as one 16-byte run from the staged V layout.
+// -----------------------------------------------------------------------------
+constexpr int kTileWaves = 8;
+constexpr int kTileThreads = kTileWaves * kWave;
+constexpr int kStageBlocks = 4;
+constexpr int kStageKeys = kStageBlocks * kBlock;   // 64
+constexpr int kTile128 = kBlock * 128 * 2;          // 4 KiB
+constexpr int kStageBytes = 2 * kStageBlocks * kTile128;
+
+__global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_tile_kernel(PrefillParams p, int ntile) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
+    constexpr int D = 128;
+    const int G = p.group;
+    const int TPW = 32 / G;  // chunk tokens per wave
+    const int QT = kTileWaves * TPW;
+    const int unit = blockIdx.x;
+    const int kvh = unit % p.n_kv;
+    const int rest = unit / p.n_kv;
+    const int qt = rest % ntile;
+    const int s = rest / ntile;
+    const int q0 = p.cu_q_lens[s];
+    const int qlen = p.cu_q_lens[s + 1] - q0;
+    const int i0 = qt * QT;
+    if (i0 >= qlen) return;
+    const int ctx = min(p.ctx[s], p.ctx_cap);
+    const int shift = ctx - qlen;  // absolute position of chunk row 0
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31;     // column (query row) of the wave's tile
+    const int half = lane >> 5;  // k-slot group
+    const int H = p.n_heads;
+
+    // the lane's query row and its Q^T operand
+    const int i = i0 + wave * TPW + n / G;
+    const bool row_ok = i < qlen;
+    const int pos = row_ok ? shift + i : -1;
+    u32x4 qop[8];
+    {
+        const uint16_t* qrow = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)(q0 + i) * H + kvh * G + n % G) * D;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            qop[kk] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * half) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    const int i_last = min(qlen, i0 + QT) - 1;
+    const int kend = shift + i_last + 1;  // keys [0, kend) are visible to some row
+    const int wfirst = i0 + wave * TPW;
+    const int wave_kmax = wfirst < qlen ? shift + min(qlen - 1, wfirst + TPW - 1) : -1;
+    const int nblk = (kend + kBlock - 1) / kBlock;
+    const int nstage = (kend + kStageKeys - 1) / kStageKeys;
+
+    const int32_t* trow = p.tables + (size_t)s * p.max_blocks;
+    const uint8_t* kpool = reinterpret_cast<const uint8_t*>(p.k_pool);
+    const uint8_t* vpool = reinterpret_cast<const uint8_t*>(p.v_pool);
+
+    // Staging. K goes straight from global memory into LDS: load j (j < 2)
+    // of wave w moves 1 KiB, block (w / 4) + 2 j, bytes (64 (w % 4) + lane)
+    // * 16 of its tile, lane by lane into consecutive 16 bytes, so a stage's
+    // K tiles land in LDS as stored. V goes through registers into a layout
+    // made for the P.V operand: the 8 keys a lane feeds one MFMA
+    // (slots 4h..4h+3 and 8+4h..8+4h+3 of one dim, h = the lane's k-slot
+    // group) form one 16-byte run at [block][h][dim], so eight consecutive
+    // lanes read 128 contiguous bytes (no bank conflicts). Thread t stages V
+    // chunks c = t and t + 512 of the stage: block c / 256, dim (c % 256) / 2,
+    // slots 8 ((c % 256) % 2) .. +7, split into two 8-byte runs.
+    const int blk_w = wave >> 2;
+    const int off = (64 * (wave & 3) + lane) * 16;
+    int win = -1, win_id = 0;
+    u32x4 vstg[2];
+    auto prefetch = [&](int st, uint8_t* buf) {
+        if ((st * kStageBlocks) >> 6 != win) {  // ids of the next 64 blocks
+            win = (st * kStageBlocks) >> 6;
+            win_id = load_ids(trow, win << 6, min(64, nblk - (win << 6)), p.num_blocks);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int blk = blk_w + 2 * j;
+            const int jb = st * kStageBlocks + blk;  // logical block (wave-uniform)
+            if (jb >= nblk) continue;                // past the last visible key (masked scores)
+            const int id = __shfl(win_id, jb & 63);
+            __builtin_amdgcn_global_load_lds(
+                kpool + ((size_t)id * p.n_kv + kvh) * kTile128 + off,
+                (__attribute__((address_space(3))) void*)(buf + blk * kTile128 + (off - lane * 16)), 16, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int c = tid + kTileThreads * j;
+            const int jb = st * kStageBlocks + (c >> 8);
+            const int id = __shfl(win_id, jb & 63);
+            vstg[j] = jb < nblk ? *reinterpret_cast<const u32x4*>(vpool + ((size_t)id * p.n_kv + kvh) * kTile128 +
+                                                                   (c & 255) * 16)
+                                : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    // Write the staged V chunks, zeroing keys at or past the context (their
+    // contents may be anything, and 0 * NaN = NaN); blocks past the last
+    // visible key were staged as zeros. K needs no care (masked scores are
+    // replaced by -inf).
+    auto commit = [&](int st, uint8_t* buf) {
+        uint8_t* vbuf = buf + kStageBlocks * kTile128;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int c = tid + kTileThreads * j;
+            const int blk = c >> 8;
+            const int d = (c & 255) >> 1;
+            const int sh = c & 1;
+            u32x4 v = vstg[j];
+            const int key0 = (st * kStageBlocks + blk) * kBlock + 8 * sh;
+            if (key0 + 8 > ctx) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = key0 + 2 * e < ctx ? 0x0000ffffu : 0u;
+                    const uint32_t hi = key0 + 2 * e + 1 < ctx ? 0xffff0000u : 0u;
+                    v[e] &= lo | hi;
+                }
+            }
+            uint8_t* row = vbuf + blk * kTile128 + d * 16 + sh * 8;
+            *reinterpret_cast<u32x2*>(row) = u32x2{v[0], v[1]};                      // slots 8sh + 0..3
+            *reinterpret_cast<u32x2*>(row + kTile128 / 2) = u32x2{v[2], v[3]};       // slots 8sh + 4..7
+        }
+    };
+
+    float m = kNegInf, l = 0.f;
+    f32x16 acc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+
+    // One stage of keys for the wave's 32 rows. The reference maximum m of a
+    // row moves only when a score exceeds it by more than kSlack (log2
+    // units); probabilities are then at most 2^kSlack, and the accumulator is
+    // rescaled only in the rare stage where some row's reference moves. When
+    // it moves it moves to the row's new maximum, whose own term is then
+    // exactly 2^0.
+    constexpr float kSlack = 8.f;
+    auto stage = [&](const uint8_t* buf, int kb, auto diag_tag) {
+        constexpr bool DIAG = decltype(diag_tag)::value;
+        const uint8_t* kst = buf;
+        const uint8_t* vst = buf + kStageBlocks * kTile128;
+        f32x16 sc[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            sc[kt] = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(
+                    kst + (2 * kt + n / 16) * kTile128 + ((2 * kk + half) * 16 + n % 16) * 16);
+                sc[kt] = mfma_32x32x16(a, qop[kk], sc[kt]);
+            }
+        }
+        // scores in log2 units, -inf past the row's position on a diagonal stage
+        float mx = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float x = sc[kt][r] * p.scale_log2;
+                if (DIAG) {
+                    const int key = kb + 32 * kt + 8 * (r / 4) + 4 * half + r % 4;
+                    x = key <= pos ? x : kNegInf;
+                }
+                sc[kt][r] = x;
+                mx = fmaxf(mx, x);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool up = mx > m + kSlack;  // false while mx is -inf
+        const float mnew = up ? mx : m;
+        const float mref = mnew == kNegInf ? 0.f : mnew;
+        const float alpha = __builtin_amdgcn_exp2f(m - mref);  // 1 unless moved (0 from -inf)
+        m = mnew;
+        u32x4 pop[2][2];
+        float psum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            float pr[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                pr[r] = __builtin_amdgcn_exp2f(sc[kt][r] - mref);
+                psum += pr[r];
+            }
+#pragma unroll
+            for (int mh = 0; mh < 2; ++mh) {
+                pop[kt][mh][0] = pack_bf16x2(pr[8 * mh + 0], pr[8 * mh + 1]);
+                pop[kt][mh][1] = pack_bf16x2(pr[8 * mh + 2], pr[8 * mh + 3]);
+                pop[kt][mh][2] = pack_bf16x2(pr[8 * mh + 4], pr[8 * mh + 5]);
+                pop[kt][mh][3] = pack_bf16x2(pr[8 * mh + 6], pr[8 * mh + 7]);
+            }
+        }
+        l = l * alpha + psum;
+        if (__any(up)) {
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+        }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const int d = 32 * dt + n;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+                for (int mh = 0; mh < 2; ++mh) {
+                    const u32x4 vop = *reinterpret_cast<const u32x4*>(vst + (2 * kt + mh) * kTile128 +
+                                                                       half * (kTile128 / 2) + d * 16);
+                    acc[dt] = mfma_32x32x16(vop, pop[kt][mh], acc[dt]);
+                }
+            }
+        }
+    };
+
+    prefetch(0, lds);
+    commit(0, lds);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's K loads have landed
+    __syncthreads();
+    for (int st = 0; st < nstage; ++st) {
+        uint8_t* buf = lds + (st & 1) * kStageBytes;
+        uint8_t* nbuf = lds + ((st + 1) & 1) * kStageBytes;
+        // the other buffer was last read before the previous barrier
+        if (st + 1 < nstage) prefetch(st + 1, nbuf);
+        const int kb = st * kStageKeys;
+        // Rows of this wave whose position is at least kb + 63 see the whole
+        // stage; only a stage on the causal diagonal needs the mask. (Rows
+        // past the chunk end never get stored.)
+        if (kb + kStageKeys - 1 <= shift + wfirst) {
+            stage(buf, kb, std::false_type{});
+        } else if (kb <= wave_kmax) {
+            stage(buf, kb, std::true_type{});
+        }
+        if (st + 1 < nstage) {
+            commit(st + 1, nbuf);
+            __builtin_amdgcn_s_waitcnt(0);  // this thread's K loads have landed
+        }
+        __syncthreads();
+    }
+
+    const float lt = l + __shfl_xor(l, 32);
+    if (!row_ok) return;
+    const float inv = 1.f / lt;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + ((size_t)(q0 + i) * H + kvh * G + n % G) * D;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            u32x2 o;
+            o[0] = pack_bf16x2(acc[dt][4 * rr + 0] * inv, acc[dt][4 * rr + 1] * inv);
+            o[1] = pack_bf16x2(acc[dt][4 * rr + 2] * inv, acc[dt][4 * rr + 3] * inv);
+            *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * rr + 4 * half) = o;
+        }
+    }
+}
+
 // fp32: one workgroup per (chunk row, KV head), the decode VALU loop over the
 // row's causal context.
 template <int D>
@@ -314,6 +582,16 @@ static hipError_t launch_mfma(const PrefillParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+static hipError_t launch_tile(const PrefillParams& p, hipStream_t stream) {
+    const int qt = kTileWaves * (32 / p.group);
+    const int ntile = (p.max_q_len + qt - 1) / qt;
+    const size_t grid = (size_t)p.num_seqs * ntile * p.n_kv;
+    if (grid == 0) return hipSuccess;
+    if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(prefill_tile_kernel, dim3((unsigned)grid), dim3(kTileThreads), 0, stream, p, ntile);
+    return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_f32(const PrefillParams& p, hipStream_t stream) {
     const size_t grid = (size_t)p.num_seqs * p.max_q_len * p.n_kv;
@@ -328,7 +606,9 @@ hipError_t launch_prefill(const PrefillParams& p, int d, int fmt, hipStream_t st
     if (d == 128) {
         switch (fmt) {
             case FMT_F32: return launch_f32<128>(p, stream);
-            case FMT_BF16: return launch_mfma<128, FMT_BF16, C>(p, stream);
+            case FMT_BF16:
+                if (32 % p.group == 0) return launch_tile(p, stream);
+                return launch_mfma<128, FMT_BF16, C>(p, stream);
             case FMT_I8: return launch_mfma<128, FMT_I8, C>(p, stream);
             case FMT_I4: return launch_mfma<128, FMT_I4, C>(p, stream);
         }
