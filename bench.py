@@ -42,7 +42,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # counter summaries under profiles/ (name of the kernel and workload)
 PROFILE_NAME = {"2": "decode_kernel_llama3_8b_bf16", "3": "decode_kernel_prefix_shared_70b_bf16",
                 "4a": "decode_kernel_quant_kv_70b_int8", "4b": "decode_kernel_quant_kv_70b_int4",
-                "5d": "decode_kernel_mixed_step_decode_bf16"}
+                "5d": "decode_kernel_mixed_step_decode_bf16", "5p": "prefill_tile_kernel_chunk2048_ctx6000_bf16"}
 
 
 def parse():
@@ -287,10 +287,11 @@ def prefill_main(a, torch, B, CONFIGS):
                    "n_heads": pre.n_heads, "n_kv_heads": pre.n_kv, "d_head": pre.d, "seed": pre.seed,
                    "decode_seqs": dec.num_seqs if mixed else 0},
         "flops_per_step": flops,
-        "roofline": {"bound": "mfma", "kernel": "prefill_kernel" if not mixed else "prefill_kernel+decode_kernel",
+        "roofline": {"bound": "mfma", "kernel": "prefill_tile_kernel" if not mixed else "prefill_tile_kernel+decode_kernel",
                      "achieved": round(flops / (k_avg * 1e-3) / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(flops / (k_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel_avg_us": round(k_avg * 1e3, 3)},
+                     "traffic": None if mixed else measured_traffic(PROFILE_NAME["5p"]),
+                     "kernel_avg_us": round(k_avg * 1e3, 3)},
     }
     if mixed:
         res["decode_algorithmic_bytes"] = int(decode_bytes(dec, 16))
