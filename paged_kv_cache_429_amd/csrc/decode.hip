@@ -47,14 +47,20 @@ constexpr int decode_waves_per_eu() {
 template <int D, int FMT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu<FMT>())))
 void decode_kernel(DecodeParams p) {
-    __shared__ WaveState<D> st;
+    // the waves' states; once merged, the partial-merge scratch
+    constexpr size_t kLds = sizeof(WaveState<D>) > kMergeFloats * sizeof(float) ? sizeof(WaveState<D>)
+                                                                               : kMergeFloats * sizeof(float);
+    constexpr int kCap = (int)(kLds / sizeof(float));
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
+    WaveState<D>& st = *reinterpret_cast<WaveState<D>*>(smem);
+    float* const scratch = reinterpret_cast<float*>(smem);
     constexpr bool F32OUT = (FMT == FMT_F32);
     if constexpr (FMT != FMT_F32) {
         if ((int)blockIdx.x < p.n_shared) {
             if (p.share_n == 2) {
-                shared_unit<D, FMT, 1, 2, F32OUT>(p, blockIdx.x, st);
+                shared_unit<D, FMT, 1, 2, F32OUT>(p, blockIdx.x, st, scratch, kCap);
             } else {
-                shared_unit<D, FMT, 1, 4, F32OUT>(p, blockIdx.x, st);
+                shared_unit<D, FMT, 1, 4, F32OUT>(p, blockIdx.x, st, scratch, kCap);
             }
             return;
         }
@@ -96,7 +102,7 @@ void decode_kernel(DecodeParams p) {
         const int id_hi = nbp > 64 ? load_ids(trow, u.b_begin + 64, nbp - 64, p.num_blocks) : 0;
         mfma_wave<D, FMT>(p, u, id_lo, id_hi, st);
     }
-    epilogue<D, F32OUT>(p, u, st);
+    epilogue<D, F32OUT>(p, u, st, scratch, kCap);
 }
 
 // Workspace: a fixed-size region of arrival counters at offset 0, then the

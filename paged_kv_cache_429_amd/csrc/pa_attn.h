@@ -131,6 +131,59 @@ struct Mfma {
         }
     }
 
+    // V operand of a pair for the decode P.V product: lane (l16, q) holds,
+    // for dim row nb*16 + l16, the 8 consecutive tokens 8 (q % 2) .. + 7 of
+    // the pair's block q / 2 -- one contiguous run of a V tile row (16, 8 or
+    // 4 bytes), so each load instruction moves 1 KiB, 512 B or 256 B.
+    static constexpr int VPDW = (FMT == FMT_BF16) ? 4 : (FMT == FMT_I8 ? 2 : 1);  // dwords per nb
+    struct VPairRaw { uint32_t w[NB * VPDW]; };
+
+    template <bool NT = true>
+    __device__ static __forceinline__ void load_v_pair(const uint8_t* tile0, const uint8_t* tile1, int lane,
+                                                       VPairRaw& r) {
+        const int l16 = lane & 15, q = lane >> 4;
+        const uint8_t* t = (q < 2) ? tile0 : tile1;
+        constexpr int ROW = 16 * BITS / 8;  // bytes of a V tile row (16 tokens of one dim)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const uint8_t* a = t + (nb * 16 + l16) * ROW + (q & 1) * (ROW / 2);
+            if (FMT == FMT_BF16) {
+                const u32x4 v = ld<NT>(reinterpret_cast<const u32x4*>(a));
+                r.w[4 * nb] = v[0];
+                r.w[4 * nb + 1] = v[1];
+                r.w[4 * nb + 2] = v[2];
+                r.w[4 * nb + 3] = v[3];
+            } else if (FMT == FMT_I8) {
+                const u32x2 v = ld<NT>(reinterpret_cast<const u32x2*>(a));
+                r.w[2 * nb] = v[0];
+                r.w[2 * nb + 1] = v[1];
+            } else {
+                r.w[nb] = ld<NT>(reinterpret_cast<const uint32_t*>(a));
+            }
+        }
+    }
+
+    // bf16 operand (8 tokens) of dim block nb
+    __device__ static __forceinline__ u32x4 v_pair_op(const VPairRaw& r, int nb) {
+        u32x4 a;
+        if (FMT == FMT_BF16) {
+            a[0] = r.w[4 * nb];
+            a[1] = r.w[4 * nb + 1];
+            a[2] = r.w[4 * nb + 2];
+            a[3] = r.w[4 * nb + 3];
+        } else if (FMT == FMT_I8) {
+            const u32x2 lo = i8x4_to_bf16x4(r.w[2 * nb]);
+            const u32x2 hi = i8x4_to_bf16x4(r.w[2 * nb + 1]);
+            a[0] = lo[0];
+            a[1] = lo[1];
+            a[2] = hi[0];
+            a[3] = hi[1];
+        } else {
+            a = i4x8_to_bf16x8(r.w[nb]);
+        }
+        return a;
+    }
+
     // bf16 values of tokens 4q..4q+3 at dim row nb*16 + lane%16
     __device__ static __forceinline__ u32x2 v_half(const VRaw& r, int nb) {
         if (FMT == FMT_BF16) {
@@ -158,7 +211,7 @@ struct KHalf {
 
 template <int D, int FMT>
 struct VHalf {
-    typename Mfma<D, FMT>::VRaw v0, v1;
+    typename Mfma<D, FMT>::VPairRaw v;
     float s0, s1;
 };
 
@@ -238,43 +291,57 @@ __device__ __forceinline__ void softmax_update(ColState<D>& c, const float* x, f
     for (int nb = 0; nb < D / 16; ++nb) c.acc[nb] *= alpha;
 }
 
-// O^T += V^T P^T for one pair. t0 is the pair's first token; V slots at or
-// past ctx (and a missing second block) are zeroed, since their contents may
-// be anything (0 * NaN = NaN). Columns with own == false contribute a zero
-// P column (their accumulator is unchanged).
+// O^T += V^T P^T for one pair. The k index of the product runs over the
+// pair's 32 tokens so that lane group q holds tokens 8 (q % 2) .. + 7 of
+// block q / 2 (the V operand is then one contiguous run of a V tile row).
+// The probabilities arrive in the S^T layout (lane group q: tokens
+// 4q..4q+3 of each block); two cross-row swaps regroup them within each
+// column. t0 is the pair's first token; V slots at or past ctx (and a
+// missing second block) are zeroed, since their contents may be anything
+// (0 * NaN = NaN). Columns with own == false contribute a zero P column
+// (their accumulator is unchanged).
 template <int D, int FMT>
 __device__ __forceinline__ void pv_update(ColState<D>& c, const VHalf<D, FMT>& r, const float* pr, int t0, int ctx,
                                           bool has1, bool own) {
     using M = Mfma<D, FMT>;
     const int q = (threadIdx.x & 63) >> 4;
-    u32x4 pop;
-    pop[0] = pack_bf16x2(pr[0] * r.s0, pr[1] * r.s0);
-    pop[1] = pack_bf16x2(pr[2] * r.s0, pr[3] * r.s0);
-    pop[2] = pack_bf16x2(pr[4] * r.s1, pr[5] * r.s1);
-    pop[3] = pack_bf16x2(pr[6] * r.s1, pr[7] * r.s1);
-    if (!own) pop = u32x4{0u, 0u, 0u, 0u};
-    const int tok0 = t0 + 4 * q;
-    const int tok1 = tok0 + kBlock;
+    // a: block 0 tokens 4q..4q+3, b: block 1 tokens 4q..4q+3 (bf16 pairs)
+    uint32_t a0 = pack_bf16x2(pr[0] * r.s0, pr[1] * r.s0);
+    uint32_t a1 = pack_bf16x2(pr[2] * r.s0, pr[3] * r.s0);
+    uint32_t b0 = pack_bf16x2(pr[4] * r.s1, pr[5] * r.s1);
+    uint32_t b1 = pack_bf16x2(pr[6] * r.s1, pr[7] * r.s1);
+    if (!own) a0 = a1 = b0 = b1 = 0u;
+    // Rows (lane groups) 0..3 of a = a@0..a@3, likewise b. After the 32-lane
+    // swap a = [a@0 a@1 b@0 b@1], b = [a@2 a@3 b@2 b@3]; after the 16-lane
+    // swap a = [a@0 a@2 b@0 b@2] (first four tokens of the group's run) and
+    // b = [a@1 a@3 b@1 b@3] (last four).
+    auto regroup = [](uint32_t& x, uint32_t& y) {
+        const auto r32 = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+        const auto r16 = __builtin_amdgcn_permlane16_swap(r32[0], r32[1], false, false);
+        x = r16[0];
+        y = r16[1];
+    };
+    regroup(a0, b0);
+    regroup(a1, b1);
+    const u32x4 pop = {a0, a1, b0, b1};
+    const int blk = q >> 1;
+    const int tok = t0 + kBlock * blk + 8 * (q & 1);  // first token of this lane group's run
     const bool tail = !has1 || t0 + 2 * kBlock > ctx;
-    uint32_t msk0[2] = {0xffffffffu, 0xffffffffu};
-    uint32_t msk1[2] = {0xffffffffu, 0xffffffffu};
+    uint32_t msk[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
     if (tail) {
+        const bool blk_ok = blk == 0 || has1;
 #pragma unroll
-        for (int w2 = 0; w2 < 2; ++w2) {
-            const int ta = tok0 + 2 * w2, tb = tok1 + 2 * w2;
-            msk0[w2] = (ta < ctx ? 0x0000ffffu : 0u) | (ta + 1 < ctx ? 0xffff0000u : 0u);
-            msk1[w2] = (has1 && tb < ctx ? 0x0000ffffu : 0u) | (has1 && tb + 1 < ctx ? 0xffff0000u : 0u);
+        for (int w = 0; w < 4; ++w) {
+            msk[w] = (blk_ok && tok + 2 * w < ctx ? 0x0000ffffu : 0u) | (blk_ok && tok + 2 * w + 1 < ctx ? 0xffff0000u : 0u);
         }
     }
 #pragma unroll
     for (int nb = 0; nb < M::NB; ++nb) {
-        const u32x2 a0 = M::v_half(r.v0, nb);
-        const u32x2 a1 = M::v_half(r.v1, nb);
-        u32x4 vop;
-        vop[0] = a0[0] & msk0[0];
-        vop[1] = a0[1] & msk0[1];
-        vop[2] = a1[0] & msk1[0];
-        vop[3] = a1[1] & msk1[1];
+        u32x4 vop = M::v_pair_op(r.v, nb);
+        vop[0] &= msk[0];
+        vop[1] &= msk[1];
+        vop[2] &= msk[2];
+        vop[3] &= msk[3];
         c.acc[nb] = mfma_16x16x32(vop, pop, c.acc[nb]);
     }
 }
@@ -319,8 +386,8 @@ __device__ __forceinline__ void issue_v_pair(const DecodeParams& p, int kvh, int
     using M = Mfma<D, FMT>;
     const int lane = threadIdx.x & 63;
     const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v_pool);
-    M::template load_v<NT>(vbase + ((size_t)i0 * p.n_kv + kvh) * M::TILE, lane, r.v0);
-    M::template load_v<NT>(vbase + ((size_t)i1 * p.n_kv + kvh) * M::TILE, lane, r.v1);
+    M::template load_v_pair<NT>(vbase + ((size_t)i0 * p.n_kv + kvh) * M::TILE,
+                                vbase + ((size_t)i1 * p.n_kv + kvh) * M::TILE, lane, r.v);
     r.s0 = r.s1 = 1.f;
     if (FMT == FMT_I8 || FMT == FMT_I4) {
         r.s0 = fp16_bits_to_f32(p.v_scales[(size_t)i0 * p.n_kv + kvh]);
@@ -583,27 +650,109 @@ __device__ __forceinline__ float load_agent(const float* p) {
     return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Log-sum-exp merge of the partials of (sequence s, KV head kvh), in
-// partition order (m and l are in log2 units):
-//   M = max_p m_p,  o = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M)
-// The partials are fetched kChunk partitions at a time with independent
-// loads (one round trip per chunk, not per partition); the running
-// (M, L, O) is rescaled when a later chunk raises the maximum.
-template <int D, bool F32OUT>
-__device__ __forceinline__ void merge_partials(const DecodeParams& p, int s, int kvh, int nparts) {
+// Log-sum-exp merge of the partials of (sequence s, KV head kvh), m and l in
+// log2 units:
+//   M = max_p m_p,  w_p = 2^(m_p - M),  o = (sum_p w_p acc_p) / (sum_p w_p l_p)
+// with both sums taken in partition order.
+// First every (head, partition) (max, sum) pair is fetched at once into LDS
+// scratch `lw` and turned into weights; then each thread fetches its
+// outputs' accumulators kChunk partitions at a time with independent loads,
+// so a merge costs two or three memory round trips, not one per output.
+constexpr int kMergeFloats = 2 * 16 * 256 + 16;  // workgroup scratch: 256 partitions at G = 16
+
+// NT threads take part (a workgroup, or one wave: NT = 64); tid is the
+// caller's index among them. lw holds `cap` floats.
+template <int NT>
+__device__ __forceinline__ void group_sync() {
+    if constexpr (NT == kThreads) {
+        __syncthreads();
+    } else {
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+template <int D, bool F32OUT, int NT>
+__device__ __forceinline__ void merge_partials(const DecodeParams& p, int s, int kvh, int nparts, float* lw, int cap,
+                                               int tid) {
     constexpr int kChunk = 8;
+    constexpr int JB = 8;  // outputs per thread per batch
     const int G = p.group;
-    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int np = nparts;
+    const size_t h0 = (size_t)s * p.n_heads + kvh * G;
+    group_sync<NT>();  // lw may still be read by the caller's previous step
+    if (2 * G * np + G <= cap) {
+        float* lm = lw;               // [G][np] max, then weight
+        float* ll = lw + G * np;      // [G][np] sum
+        float* lsum = lw + 2 * G * np;  // [G] total weighted sum
+        for (int t = tid; t < G * np; t += NT) {
+            const int g = t / np, q = t - g * np;
+            const float* ml = p.part_ml + ((h0 + g) * p.pmax + q) * 2;
+            const float mv = load_agent(ml);
+            const float lv = load_agent(ml + 1);
+            lm[t] = mv;
+            ll[t] = lv;
+        }
+        group_sync<NT>();
+        for (int g = tid; g < G; g += NT) {
+            float M = kNegInf;
+            for (int q = 0; q < np; ++q) M = fmaxf(M, lm[g * np + q]);
+            float L = 0.f;
+            for (int q = 0; q < np; ++q) {
+                const float e = __builtin_amdgcn_exp2f(lm[g * np + q] - M);
+                L += e * ll[g * np + q];
+                lm[g * np + q] = e;
+            }
+            lsum[g] = L;
+        }
+        group_sync<NT>();
+        for (int i0 = 0; i0 < G * D; i0 += JB * NT) {
+            float O[JB];
+#pragma unroll
+            for (int j = 0; j < JB; ++j) O[j] = 0.f;
+            for (int q0 = 0; q0 < np; q0 += kChunk) {
+                float a[JB][kChunk];
+#pragma unroll
+                for (int j = 0; j < JB; ++j) {
+                    const int idx = i0 + tid + j * NT;
+                    const int g = idx / D, d = idx - g * D;
+#pragma unroll
+                    for (int c = 0; c < kChunk; ++c) {
+                        a[j][c] = (idx < G * D && q0 + c < np)
+                                      ? load_agent(p.part_acc + ((h0 + g) * p.pmax + q0 + c) * D + d)
+                                      : 0.f;
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < JB; ++j) {
+                    const int idx = i0 + tid + j * NT;
+                    const int g = min(idx / D, G - 1);
+#pragma unroll
+                    for (int c = 0; c < kChunk; ++c) {
+                        if (q0 + c < np) O[j] += lm[g * np + q0 + c] * a[j][c];
+                    }
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < JB; ++j) {
+                const int idx = i0 + tid + j * NT;
+                if (idx < G * D) store_out<D, F32OUT>(p, h0 * D + idx, O[j] / lsum[idx / D]);
+            }
+        }
+        return;
+    }
+    // very many partitions: one output per thread at a time, the running
+    // (M, L, O) rescaled when a later chunk raises the maximum
+    for (int idx = tid; idx < G * D; idx += NT) {
         const int g = idx / D, d = idx - g * D;
-        const size_t h = (size_t)s * p.n_heads + kvh * G + g;
-        const float* ml = p.part_ml + h * p.pmax * 2;
-        const float* acc = p.part_acc + h * p.pmax * D + d;
+        const float* ml = p.part_ml + (h0 + g) * p.pmax * 2;
+        const float* acc = p.part_acc + (h0 + g) * p.pmax * D + d;
         float M = kNegInf, L = 0.f, O = 0.f;
-        for (int p0 = 0; p0 < nparts; p0 += kChunk) {
+        for (int p0 = 0; p0 < np; p0 += kChunk) {
             float mv[kChunk], lv[kChunk], av[kChunk];
 #pragma unroll
             for (int c = 0; c < kChunk; ++c) {
-                const bool ok = p0 + c < nparts;
+                const bool ok = p0 + c < np;
                 mv[c] = ok ? load_agent(ml + 2 * (p0 + c)) : kNegInf;
                 lv[c] = ok ? load_agent(ml + 2 * (p0 + c) + 1) : 0.f;
                 av[c] = ok ? load_agent(acc + (size_t)(p0 + c) * D) : 0.f;
@@ -622,7 +771,7 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& p, int s, int
             }
             M = Mc;
         }
-        store_out<D, F32OUT>(p, h * D + d, O / L);
+        store_out<D, F32OUT>(p, h0 * D + idx, O / L);
     }
 }
 
@@ -677,8 +826,10 @@ __device__ __forceinline__ bool arrive(const DecodeParams& p, int s, int kvh, in
 // Epilogue of a (sequence, KV head, partition) workgroup: merge the waves,
 // store, and if this was the last partition of a split sequence to arrive,
 // merge all its partials.
+// merge_scratch: `cap` floats of LDS, which may alias st.
 template <int D, bool F32OUT>
-__device__ __forceinline__ void epilogue(const DecodeParams& p, const Unit& u, WaveState<D>& st) {
+__device__ __forceinline__ void epilogue(const DecodeParams& p, const Unit& u, WaveState<D>& st,
+                                         float* merge_scratch, int cap) {
     __syncthreads();
     const int G = p.group;
     merge_waves_store<D, F32OUT>(p, st, G, u.part, [&](int col, int& s, int& qh, int& np) {
@@ -696,7 +847,7 @@ __device__ __forceinline__ void epilogue(const DecodeParams& p, const Unit& u, W
     if (threadIdx.x == 0) last = arrive(p, u.s, u.kvh, u.nparts);
     __syncthreads();
     if (!last) return;
-    merge_partials<D, F32OUT>(p, u.s, u.kvh, u.nparts);
+    merge_partials<D, F32OUT, kThreads>(p, u.s, u.kvh, u.nparts, merge_scratch, cap, threadIdx.x);
 }
 
 // -----------------------------------------------------------------------------
@@ -750,7 +901,8 @@ __device__ __forceinline__ bool group_shares(const DecodeParams& p, int s0, int 
 }
 
 template <int D, int FMT, int CS, int NS, bool F32OUT>
-__device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, WaveState<D>& st) {
+__device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, WaveState<D>& st, float* merge_scratch,
+                                            int cap) {
     using M = Mfma<D, FMT>;
     const int kvh = unit % p.n_kv;
     const int rest = unit / p.n_kv;
@@ -965,7 +1117,8 @@ __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, Wav
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-        if (i < NS && last[i]) merge_partials<D, F32OUT>(p, s0 + i, kvh, nparts[i]);
+        if (i < NS && last[i])
+            merge_partials<D, F32OUT, kThreads>(p, s0 + i, kvh, nparts[i], merge_scratch, cap, threadIdx.x);
     }
 }
 

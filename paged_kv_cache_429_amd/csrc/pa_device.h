@@ -103,4 +103,32 @@ __device__ __forceinline__ T readlane(T v, int lane) {
     return __builtin_amdgcn_readlane(v, lane);
 }
 
+// Direct global-to-LDS load of 16 bytes per lane: lane i's bytes land at LDS
+// byte address lds_base + 16 i (lds_base wave-uniform). It is issued as
+// inline assembly so that the compiler does not make every later LDS read
+// wait for it (it cannot tell which LDS bytes the load writes, and would
+// otherwise drain all such loads before the next LDS read, which defeats
+// multi-buffering); the caller orders it with lds_wait_barrier.
+// M0 (which carries the LDS address) is saved and restored around it.
+__device__ __forceinline__ void lds_dma16(const void* src, const void* lds_dst) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint8_t*)lds_dst)));
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(base)
+        : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (loads complete in order, so every earlier direct-to-LDS load has landed),
+// then a workgroup barrier. A compiler memory barrier as well: no memory
+// access moves across it.
+template <int N>
+__device__ __forceinline__ void lds_wait_barrier() {
+    static_assert(N >= 0 && N < 16, "vmcnt");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
 }  // namespace pa

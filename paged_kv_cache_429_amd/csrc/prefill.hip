@@ -351,24 +351,22 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
             const int jb = st * kStageBlocks + blk;  // logical block (wave-uniform)
             if (jb >= nblk) continue;                // past the last visible key (masked scores)
             const int id = __shfl(win_id, jb & 63);
-            __builtin_amdgcn_global_load_lds(
-                kpool + ((size_t)id * p.n_kv + kvh) * kTile128 + off,
-                (__attribute__((address_space(3))) void*)(buf + blk * kTile128 + (off - lane * 16)), 16, 0, 0);
+            lds_dma16(kpool + ((size_t)id * p.n_kv + kvh) * kTile128 + off, buf + blk * kTile128 + (off - lane * 16));
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int c = tid + kTileThreads * j;
             const int jb = st * kStageBlocks + (c >> 8);
+            // past the last visible block the window holds id 0 (a valid
+            // block), whose keys the commit masks out
             const int id = __shfl(win_id, jb & 63);
-            vstg[j] = jb < nblk ? *reinterpret_cast<const u32x4*>(vpool + ((size_t)id * p.n_kv + kvh) * kTile128 +
-                                                                   (c & 255) * 16)
-                                : u32x4{0u, 0u, 0u, 0u};
+            vstg[j] = *reinterpret_cast<const u32x4*>(vpool + ((size_t)id * p.n_kv + kvh) * kTile128 + (c & 255) * 16);
         }
     };
     // Write the staged V chunks, zeroing keys at or past the context (their
-    // contents may be anything, and 0 * NaN = NaN); blocks past the last
-    // visible key were staged as zeros. K needs no care (masked scores are
-    // replaced by -inf).
+    // contents may be anything, and 0 * NaN = NaN), which covers the blocks
+    // past the last visible one. K needs no care (masked scores are replaced
+    // by -inf).
     auto commit = [&](int st, uint8_t* buf) {
         uint8_t* vbuf = buf + kStageBlocks * kTile128;
 #pragma unroll
@@ -567,7 +565,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(PrefillParams pp)
     for (int idx = threadIdx.x; idx < p.group * D; idx += kThreads) qs[idx] = qg[idx];
     __syncthreads();
     f32_wave<D>(p, u, pp.tables + (size_t)s * pp.max_blocks, st, qs);
-    epilogue<D, true>(p, u, st);
+    epilogue<D, true>(p, u, st, reinterpret_cast<float*>(&st), (int)(sizeof(st) / sizeof(float)));
 }
 
 template <int D, int FMT, int C>

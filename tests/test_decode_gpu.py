@@ -93,16 +93,19 @@ def test_shared_equals_private_bitexact(lib):
     assert_close(dev_to_f64(a), oracle_decode(c), "bf16", "shared")
 
 
-# Clusters of sequences sharing prefixes of several lengths: groups of
-# consecutive sequences that share the first pair of a partition go through
-# the shared-prefix workgroups, the rest through the per-sequence path. Some
-# clusters have odd sizes (groups straddle clusters), odd shared-block counts
-# (a shared run ends inside a pair), and members shorter than the prefix.
+# Clusters of sequences sharing prefixes of several lengths. Shared-prefix
+# workgroups take 4 * 16 / G consecutive sequences (8 at G = 8, 16 at G = 4)
+# that all share the first pair of a partition; everything else goes through
+# the per-sequence path. The clusters are sized so that, at both group sizes,
+# some workgroups fall wholly inside a cluster, some straddle two clusters,
+# and some hold a member shorter than its cluster's prefix; prefixes have odd
+# block counts, and members end exactly at, one token past, and well past
+# their prefix.
 CLUSTERS = [
-    (90, [1500, 1441, 1600, 1700, 1488, 1501]),
-    (57, [920, 1000, 912, 950, 930]),
-    (31, [600, 300, 497, 498]),
-    (12, [150, 190]),
+    (90, [1500, 1441, 1600, 1700, 1488, 1501, 1450, 1520, 1444, 1499, 1600, 1690, 1455, 1470, 1530, 1510]),
+    (57, [920, 1000, 912, 950, 930, 917, 999, 1010, 960, 925, 940, 913]),
+    (31, [600, 497, 498, 520, 610, 700, 505, 499, 530, 640, 512, 496, 800, 560, 590, 620, 505, 777, 515, 300]),
+    (12, [150, 190, 200, 170, 199, 160, 210, 180]),
     (0, [700, 333, 64]),
 ]
 
