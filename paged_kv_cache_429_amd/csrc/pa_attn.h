@@ -3,6 +3,8 @@
 // log-sum-exp epilogue.
 #pragma once
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -458,6 +460,103 @@ __device__ __forceinline__ int pair_run(const DecodeParams& p, int kvh, const u3
     return k + kWaves;
 }
 
+// Pairs whose loads are in flight ahead of the one being computed in the
+// per-sequence path: two for int4, whose pairs are small (4 KiB), so that a
+// CU keeps more bytes in flight; one for bf16 and int8 (int8 runs out of
+// registers at two). The prefetch distance changes when a pair's loads are
+// issued, never its arithmetic.
+template <int FMT>
+constexpr int prefetch_pairs() {
+    return FMT == FMT_I4 ? 2 : 1;
+}
+
+// pair_run with two pairs in flight: the n >= 1 pairs k, k + 4, ...,
+// k + 4 (n - 1) of one wave. The loads of pair i + PD (PD = 1 or 2) go out while pair
+// i is computed: its K once pair i's scores are taken, its V once pair i's
+// P.V is done, into the register slot pair i used. Steady-state loads are
+// unconditional and the last pairs are peeled off, so the wait before each
+// use covers only the half it reads.
+//   ids(k, i0, i1)          physical ids of the pair's blocks
+//   geo(k, t0, ctx, has1)   first token, the context that masks it, and
+//                           whether its second block exists
+// NT selects the streaming load policy; lanes with own == false (columns of
+// another sequence) see -inf scores and a zero P column, which leave their
+// state unchanged. Returns the first pair after the run.
+template <int D, int FMT, bool NT, int PD, typename Ids, typename Geo>
+__device__ __forceinline__ int pair_run_deep(const DecodeParams& p, int kvh, const u32x4* qop, ColState<D>& cs,
+                                             int k, int n, Ids ids, Geo geo, bool own = true) {
+    static_assert(PD == 1 || PD == 2, "prefetch distance");
+    const int q = (threadIdx.x & 63) >> 4;
+    KHalf<D, FMT> kr[PD];
+    VHalf<D, FMT> vr[PD];
+    auto pair_of = [&](int i) { return k + i * kWaves; };
+    // pair i into register slot SLOT
+    auto issue = [&](auto slot_tag, int i) {
+        constexpr int SLOT = decltype(slot_tag)::value;
+        int i0, i1;
+        ids(pair_of(i), i0, i1);
+        issue_k_pair<D, FMT, NT>(p, kvh, i0, i1, kr[SLOT]);
+        issue_v_pair<D, FMT, NT>(p, kvh, i0, i1, vr[SLOT]);
+    };
+    // pair i from slot SLOT; if PREFETCH, pair pf goes into the same slot
+    auto step = [&](auto slot_tag, auto prefetch_tag, int i, int pf) {
+        constexpr int SLOT = decltype(slot_tag)::value;
+        constexpr bool PREFETCH = decltype(prefetch_tag)::value;
+        int t0, ctx;
+        bool has1;
+        geo(pair_of(i), t0, ctx, has1);
+        f32x4 s0, s1;
+        pair_scores<D, FMT>(kr[SLOT], qop, s0, s1);
+        // take the K scales before the prefetch replaces them
+        const float c0 = p.scale_log2 * kr[SLOT].s0;
+        const float c1 = p.scale_log2 * kr[SLOT].s1;
+        int n0 = 0, n1 = 0;
+        if (PREFETCH) {
+            ids(pair_of(pf), n0, n1);
+            issue_k_pair<D, FMT, NT>(p, kvh, n0, n1, kr[SLOT]);
+        }
+        float x[8], pr[8];
+        scale_mask(s0, s1, c0, c1, t0 + 4 * q, ctx, has1, x);
+        if (!own) {  // a column of another sequence: no update
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = kNegInf;
+        }
+        softmax_update(cs, x, pr);
+        pv_update<D, FMT>(cs, vr[SLOT], pr, t0, ctx, has1, own);
+        if (PREFETCH) issue_v_pair<D, FMT, NT>(p, kvh, n0, n1, vr[SLOT]);
+    };
+    constexpr std::integral_constant<int, 0> s0_{};
+    constexpr std::integral_constant<int, PD - 1> s1_{};
+    constexpr std::true_type yes{};
+    constexpr std::false_type no{};
+    if constexpr (PD == 1) {
+        issue(s0_, 0);
+        int i = 0;
+        for (; i + 1 < n; ++i) step(s0_, yes, i, i + 1);
+        step(s0_, no, i, 0);
+    } else {
+        issue(s0_, 0);
+        if (n > 1) issue(s1_, 1);
+        int i = 0;
+        for (; i + 3 < n; i += 2) {
+            step(s0_, yes, i, i + 2);
+            step(s1_, yes, i + 1, i + 3);
+        }
+        // one to three pairs left
+        if (i + 2 < n) {
+            step(s0_, yes, i, i + 2);
+            step(s1_, no, i + 1, 0);
+            step(s0_, no, i + 2, 0);
+        } else if (i + 1 < n) {
+            step(s0_, no, i, 0);
+            step(s1_, no, i + 1, 0);
+        } else {
+            step(s0_, no, i, 0);
+        }
+    }
+    return k + n * kWaves;
+}
+
 // One wave of a (sequence, KV head, partition) workgroup: pairs wave,
 // wave + 4, ... of the partition, the G query heads of the KV head in
 // columns 0..G-1.
@@ -477,19 +576,21 @@ __device__ __forceinline__ void mfma_wave(const DecodeParams& p, const Unit& u, 
     const int nb_part = u.b_end - u.b_begin;
     const int npairs = (nb_part + 1) >> 1;
     if (wave < npairs) {
-        pair_run<D, FMT, true>(
-            p, u.kvh, qop, cs, wave,
-            // a missing second block repeats the first, which is then masked out
-            [&](int k, int& i0, int& i1) {
-                i0 = tile_id(id_lo, id_hi, 2 * k);
-                i1 = (2 * k + 1) < nb_part ? tile_id(id_lo, id_hi, 2 * k + 1) : i0;
-            },
-            [&](int k) { return k < npairs; },
-            [&](int k, int& t0, int& ctx, bool& has1) {
-                t0 = (u.b_begin + 2 * k) * kBlock;
-                ctx = u.ctx;
-                has1 = 2 * k + 1 < nb_part;
-            });
+        // a missing second block repeats the first, which is then masked out
+        auto ids = [&](int k, int& i0, int& i1) {
+            i0 = tile_id(id_lo, id_hi, 2 * k);
+            i1 = (2 * k + 1) < nb_part ? tile_id(id_lo, id_hi, 2 * k + 1) : i0;
+        };
+        auto geo = [&](int k, int& t0, int& ctx, bool& has1) {
+            t0 = (u.b_begin + 2 * k) * kBlock;
+            ctx = u.ctx;
+            has1 = 2 * k + 1 < nb_part;
+        };
+        if constexpr (prefetch_pairs<FMT>() == 2) {
+            pair_run_deep<D, FMT, true, 2>(p, u.kvh, qop, cs, wave, (npairs - wave + kWaves - 1) / kWaves, ids, geo);
+        } else {
+            pair_run<D, FMT, true>(p, u.kvh, qop, cs, wave, ids, [&](int k) { return k < npairs; }, geo);
+        }
     }
     col_to_lds(cs, st, wave);
 }

@@ -326,35 +326,37 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
     const uint8_t* kpool = reinterpret_cast<const uint8_t*>(p.k_pool);
     const uint8_t* vpool = reinterpret_cast<const uint8_t*>(p.v_pool);
 
-    // Staging. K goes straight from global memory into LDS: load j (j < 2)
-    // of wave w moves 1 KiB, block (w / 4) + 2 j, bytes (64 (w % 4) + lane)
-    // * 16 of its tile, lane by lane into consecutive 16 bytes, so a stage's
-    // K tiles land in LDS as stored. V goes through registers into a layout
+    // Staging. K goes straight from global memory into LDS: load j of wave w
+    // moves 1 KiB piece c = w + W j of the stage (W waves): block c / 4,
+    // bytes (64 (c % 4) + lane) * 16 of its tile, lane by lane into
+    // consecutive 16 bytes, so a stage's K tiles land in LDS as stored. V goes through registers into a layout
     // made for the P.V operand: the 8 keys a lane feeds one MFMA
     // (slots 4h..4h+3 and 8+4h..8+4h+3 of one dim, h = the lane's k-slot
     // group) form one 16-byte run at [block][h][dim], so eight consecutive
     // lanes read 128 contiguous bytes (no bank conflicts). Thread t stages V
-    // chunks c = t and t + 512 of the stage: block c / 256, dim (c % 256) / 2,
-    // slots 8 ((c % 256) % 2) .. +7, split into two 8-byte runs.
-    const int blk_w = wave >> 2;
-    const int off = (64 * (wave & 3) + lane) * 16;
+    // chunks c = t, t + T, ... of the stage (T threads): block c / 256, dim
+    // (c % 256) / 2, slots 8 ((c % 256) % 2) .. +7, split into two 8-byte runs.
+    constexpr int KLD = kStageBlocks * kTile128 / 1024 / kTileWaves;  // K loads per wave per stage
+    constexpr int VCH = kStageBlocks * kTile128 / 16 / kTileThreads;  // V chunks per thread per stage
     int win = -1, win_id = 0;
-    u32x4 vstg[2];
+    u32x4 vstg[VCH];
     auto prefetch = [&](int st, uint8_t* buf) {
         if ((st * kStageBlocks) >> 6 != win) {  // ids of the next 64 blocks
             win = (st * kStageBlocks) >> 6;
             win_id = load_ids(trow, win << 6, min(64, nblk - (win << 6)), p.num_blocks);
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int blk = blk_w + 2 * j;
+        for (int j = 0; j < KLD; ++j) {
+            const int c = wave + kTileWaves * j;     // 1 KiB piece of the stage's K
+            const int blk = c >> 2;
+            const int off = (64 * (c & 3) + lane) * 16;
             const int jb = st * kStageBlocks + blk;  // logical block (wave-uniform)
             if (jb >= nblk) continue;                // past the last visible key (masked scores)
             const int id = __shfl(win_id, jb & 63);
             lds_dma16(kpool + ((size_t)id * p.n_kv + kvh) * kTile128 + off, buf + blk * kTile128 + (off - lane * 16));
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < VCH; ++j) {
             const int c = tid + kTileThreads * j;
             const int jb = st * kStageBlocks + (c >> 8);
             // past the last visible block the window holds id 0 (a valid
@@ -370,7 +372,7 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
     auto commit = [&](int st, uint8_t* buf) {
         uint8_t* vbuf = buf + kStageBlocks * kTile128;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < VCH; ++j) {
             const int c = tid + kTileThreads * j;
             const int blk = c >> 8;
             const int d = (c & 255) >> 1;
@@ -408,6 +410,9 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
         const uint8_t* kst = buf;
         const uint8_t* vst = buf + kStageBlocks * kTile128;
         f32x16 sc[2];
+        // MFMA issue at raised wave priority: the two waves of a SIMD drift
+        // apart, so one's softmax overlaps the other's MFMAs
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             sc[kt] = f32x16{};
@@ -418,6 +423,7 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
                 sc[kt] = mfma_32x32x16(a, qop[kk], sc[kt]);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         // scores in log2 units, -inf past the row's position on a diagonal stage
         float mx = kNegInf;
 #pragma unroll
@@ -462,6 +468,7 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
         }
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
             const int d = 32 * dt + n;
@@ -475,6 +482,7 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
                 }
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     };
 
     prefetch(0, lds);
