@@ -8,9 +8,9 @@
 // found through the sequence's block table.
 //
 // Work decomposition. One workgroup (4 waves) per (sequence, KV head,
-// context partition); the KV head is the fastest-varying index, so with 8 KV
-// heads each head's workgroups land on one XCD (workgroups are dealt to the
-// 8 XCDs round-robin). A partition is `pb` consecutive logical blocks; the
+// context partition), partitions in descending order; the KV head is the
+// fastest-varying index, so with 8 KV heads each head's workgroups land on
+// one XCD (workgroups are dealt to the 8 XCDs round-robin). A partition is `pb` consecutive logical blocks; the
 // waves take pairs of blocks round-robin. All G query heads of the KV head
 // are processed together, so each K/V tile is read from HBM once per KV head
 // (GQA batching, "KV cache, GQA, paging and continuous batching", section
@@ -69,8 +69,12 @@ void decode_kernel(DecodeParams p) {
     const int unit = blockIdx.x - p.n_shared;
     u.kvh = unit % p.n_kv;
     const int rest = unit / p.n_kv;
-    u.part = rest % p.pmax;
-    u.s = rest / p.pmax;
+    // Highest partitions first, partition 0 of every sequence last: the
+    // last round of workgroups then holds whole short sequences and full
+    // first partitions, of similar size, instead of a random mix (the
+    // order changes nothing but when a unit runs).
+    u.s = rest % p.num_seqs;
+    u.part = p.pmax - 1 - rest / p.num_seqs;
     u.ctx = min(p.ctx[u.s], p.ctx_cap);
     if (u.ctx <= 0) {
         if (u.part == 0) {
