@@ -95,6 +95,20 @@ struct Mfma {
         }
     }
 
+    // The decode path takes int4 codes offset by kOff = 136 (two ALU ops per
+    // element instead of an exact widening); the scores subtract kOff * sum(q)
+    // and the accumulator kOff * sum(P), both in fp32.
+    static constexpr bool kOffset = (FMT == FMT_I4);
+    static constexpr float kOff = 136.f;
+
+    __device__ static __forceinline__ u32x4 k_operand_dec(const KRaw& r, int kk) {
+        if constexpr (kOffset) {
+            return i4x8_to_bf16x8_off136(r.w[kk]);
+        } else {
+            return k_operand(r, kk);
+        }
+    }
+
     __device__ static __forceinline__ u32x4 k_operand(const KRaw& r, int kk) {
         u32x4 a;
         if (FMT == FMT_BF16) {
@@ -165,7 +179,7 @@ struct Mfma {
         }
     }
 
-    // bf16 operand (8 tokens) of dim block nb
+    // bf16 operand (8 tokens) of dim block nb; int4 comes offset by kOff
     __device__ static __forceinline__ u32x4 v_pair_op(const VPairRaw& r, int nb) {
         u32x4 a;
         if (FMT == FMT_BF16) {
@@ -181,7 +195,7 @@ struct Mfma {
             a[2] = hi[0];
             a[3] = hi[1];
         } else {
-            a = i4x8_to_bf16x8(r.w[nb]);
+            a = i4x8_to_bf16x8_off136(r.w[nb]);  // offset by kOff (see k_operand_dec)
         }
         return a;
     }
@@ -224,12 +238,14 @@ template <int D>
 struct ColState {
     float m, l;
     f32x4 acc[D / 16];
+    float corr;  // offset formats: this lane's share of kOff * sum(P), rescaled with acc
 };
 
 template <int D>
 __device__ __forceinline__ void col_init(ColState<D>& c) {
     c.m = kNegInf;
     c.l = 0.f;
+    c.corr = 0.f;
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) c.acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
@@ -249,8 +265,8 @@ __device__ __forceinline__ void pair_scores(const KHalf<D, FMT>& r, const u32x4*
     s1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < M::KSTEPS; ++kk) {
-        s0 = mfma_16x16x32(M::k_operand(r.k0, kk), qop[kk], s0);
-        s1 = mfma_16x16x32(M::k_operand(r.k1, kk), qop[kk], s1);
+        s0 = mfma_16x16x32(M::k_operand_dec(r.k0, kk), qop[kk], s0);
+        s1 = mfma_16x16x32(M::k_operand_dec(r.k1, kk), qop[kk], s1);
     }
 }
 
@@ -289,6 +305,7 @@ __device__ __forceinline__ void softmax_update(ColState<D>& c, const float* x, f
         psum += pr[i];
     }
     c.l = c.l * alpha + psum;
+    c.corr *= alpha;
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) c.acc[nb] *= alpha;
 }
@@ -313,6 +330,12 @@ __device__ __forceinline__ void pv_update(ColState<D>& c, const VHalf<D, FMT>& r
     uint32_t b0 = pack_bf16x2(pr[4] * r.s1, pr[5] * r.s1);
     uint32_t b1 = pack_bf16x2(pr[6] * r.s1, pr[7] * r.s1);
     if (!own) a0 = a1 = b0 = b1 = 0u;
+    if constexpr (M::kOffset) {  // kOff * the P values exactly as the MFMA sees them
+        auto lo = [](uint32_t x) { return __uint_as_float(x << 16); };
+        auto hi = [](uint32_t x) { return __uint_as_float(x & 0xffff0000u); };
+        const float ps = ((lo(a0) + hi(a0)) + (lo(a1) + hi(a1))) + ((lo(b0) + hi(b0)) + (lo(b1) + hi(b1)));
+        c.corr += M::kOff * ps;
+    }
     // Rows (lane groups) 0..3 of a = a@0..a@3, likewise b. After the 32-lane
     // swap a = [a@0 a@1 b@0 b@1], b = [a@2 a@3 b@2 b@3]; after the 16-lane
     // swap a = [a@0 a@2 b@0 b@2] (first four tokens of the group's run) and
@@ -350,7 +373,7 @@ __device__ __forceinline__ void pv_update(ColState<D>& c, const VHalf<D, FMT>& r
 
 // Write one wave's column states to LDS slot `wave` (row sums completed
 // over the four lane groups of each column).
-template <int D>
+template <int D, bool OFFSET = false>
 __device__ __forceinline__ void col_to_lds(ColState<D>& c, WaveState<D>& st, int wave) {
     const int lane = threadIdx.x & 63;
     const int g = lane & 15;
@@ -358,6 +381,13 @@ __device__ __forceinline__ void col_to_lds(ColState<D>& c, WaveState<D>& st, int
     float l = c.l;
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
+    if constexpr (OFFSET) {  // remove the operand offset's share of the accumulator
+        float corr = c.corr;
+        corr += __shfl_xor(corr, 16);
+        corr += __shfl_xor(corr, 32);
+#pragma unroll
+        for (int nb = 0; nb < D / 16; ++nb) c.acc[nb] -= corr;
+    }
     if (q == 0) {
         st.m[wave][g] = c.m;
         st.l[wave][g] = l;
@@ -397,6 +427,29 @@ __device__ __forceinline__ void issue_v_pair(const DecodeParams& p, int kvh, int
     }
 }
 
+// kOff * (sum of the column's Q^T operand values) for the offset formats,
+// else 0: the score correction of offset K codes.
+template <int D, int FMT>
+__device__ __forceinline__ float q_offset(const u32x4* qop) {
+    using M = Mfma<D, FMT>;
+    if constexpr (!M::kOffset) {
+        return 0.f;
+    } else {
+        float sum = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < M::KSTEPS; ++kk) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sum += __uint_as_float(qop[kk][e] << 16);
+                sum += __uint_as_float(qop[kk][e] & 0xffff0000u);
+            }
+        }
+        sum += __shfl_xor(sum, 16);
+        sum += __shfl_xor(sum, 32);
+        return M::kOff * sum;
+    }
+}
+
 // Q^T operand of column `col` (query head qh of sequence s), eight dims per
 // k-step; zero for an unused column.
 template <int D, int FMT>
@@ -425,6 +478,7 @@ template <int D, int FMT, bool NT, typename Ids, typename More, typename Geo>
 __device__ __forceinline__ int pair_run(const DecodeParams& p, int kvh, const u32x4* qop, ColState<D>& cs, int k,
                                         Ids ids, More more, Geo geo, bool own = true) {
     const int q = (threadIdx.x & 63) >> 4;
+    const float qoff = q_offset<D, FMT>(qop);
     KHalf<D, FMT> kr;
     VHalf<D, FMT> vr;
     auto step = [&](int kk, bool prefetch) {
@@ -442,6 +496,10 @@ __device__ __forceinline__ int pair_run(const DecodeParams& p, int kvh, const u3
             issue_k_pair<D, FMT, NT>(p, kvh, n0, n1, kr);
         }
         float x[8], pr[8];
+        if constexpr (Mfma<D, FMT>::kOffset) {
+            s0 -= qoff;
+            s1 -= qoff;
+        }
         scale_mask(s0, s1, c0, c1, t0 + 4 * q, ctx, has1, x);
         if (!own) {  // a column of another sequence: no update
 #pragma unroll
@@ -487,6 +545,7 @@ __device__ __forceinline__ int pair_run_deep(const DecodeParams& p, int kvh, con
                                              int k, int n, Ids ids, Geo geo, bool own = true) {
     static_assert(PD == 1 || PD == 2, "prefetch distance");
     const int q = (threadIdx.x & 63) >> 4;
+    const float qoff = q_offset<D, FMT>(qop);
     KHalf<D, FMT> kr[PD];
     VHalf<D, FMT> vr[PD];
     auto pair_of = [&](int i) { return k + i * kWaves; };
@@ -516,6 +575,10 @@ __device__ __forceinline__ int pair_run_deep(const DecodeParams& p, int kvh, con
             issue_k_pair<D, FMT, NT>(p, kvh, n0, n1, kr[SLOT]);
         }
         float x[8], pr[8];
+        if constexpr (Mfma<D, FMT>::kOffset) {
+            s0 -= qoff;
+            s1 -= qoff;
+        }
         scale_mask(s0, s1, c0, c1, t0 + 4 * q, ctx, has1, x);
         if (!own) {  // a column of another sequence: no update
 #pragma unroll
@@ -592,7 +655,7 @@ __device__ __forceinline__ void mfma_wave(const DecodeParams& p, const Unit& u, 
             pair_run<D, FMT, true>(p, u.kvh, qop, cs, wave, ids, [&](int k) { return k < npairs; }, geo);
         }
     }
-    col_to_lds(cs, st, wave);
+    col_to_lds<D, Mfma<D, FMT>::kOffset>(cs, st, wave);
 }
 
 // -----------------------------------------------------------------------------
@@ -960,8 +1023,8 @@ __device__ __forceinline__ void epilogue(const DecodeParams& p, const Unit& u, W
 // A group of NS = 16/G consecutive sequences (G = 4 or 8) whose tables name
 // the same physical blocks for the first pair of a partition, all full, is
 // processed by one workgroup for that (KV head, partition): the G query
-// heads of the NS sequences fill the 16 MFMA columns (CS = 1 column set per
-// wave; the template allows more where registers permit). A block pair that every sequence
+// heads of the NS sequences fill the 16 MFMA columns (one column set per
+// wave). A block pair that every sequence
 // of the group shares (same ids, full in every sequence) is loaded once, with
 // the cache-friendly policy so that the other groups' workgroups find it in
 // L2, and feeds all columns; any other pair is loaded per sequence and feeds
@@ -1004,6 +1067,7 @@ __device__ __forceinline__ bool group_shares(const DecodeParams& p, int s0, int 
 template <int D, int FMT, int CS, int NS, bool F32OUT>
 __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, WaveState<D>& st, float* merge_scratch,
                                             int cap) {
+    static_assert(CS == 1, "one column set per wave");
     using M = Mfma<D, FMT>;
     const int kvh = unit % p.n_kv;
     const int rest = unit / p.n_kv;
@@ -1047,10 +1111,6 @@ __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, Wav
         load_qop<D, FMT>(p, s0 + c * TPG + owner, kvh * G + col % G, true, qop[c]);
         col_init(cst[c]);
     }
-    auto qget = [&](int c, u32x4* qr) {
-#pragma unroll
-        for (int kk = 0; kk < M::KSTEPS; ++kk) qr[kk] = qop[c][kk];
-    };
     // Pair k is shared when every sequence of the group holds both its
     // blocks, full, at the same physical ids.
     auto shared_pair = [&](int k) {
@@ -1069,7 +1129,7 @@ __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, Wav
     };
 
     int k = wave;
-    if (CS == 1 && k < npmax && shared_pair(k)) {
+    if (k < npmax && shared_pair(k)) {
         // the leading run of shared pairs, pipelined like the per-sequence
         // path and with the same per-column operations (every token of a
         // shared pair is in context)
@@ -1086,7 +1146,7 @@ __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, Wav
                 has1 = true;
             });
     }
-    if (CS == 1) {
+    {
         // The rest, sequence by sequence: each sequence's remaining pairs
         // (in order) as one pipelined run that updates only its columns.
 #pragma unroll
@@ -1107,93 +1167,13 @@ __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, Wav
                     owner == i);
             }
         }
-    } else {
-        // the rest, one pair at a time (shared or not)
-        for (; k < npmax; k += kWaves) {
-            const int t0 = (b + 2 * k) * kBlock;
-            const int a0 = tile_id(my_id[0], my_hi[0], 2 * k);
-            const int a1 = tile_id(my_id[0], my_hi[0], 2 * k + 1);
-            if (shared_pair(k)) {
-                // one load of the pair feeds every column set
-                KHalf<D, FMT> kr;
-                issue_k_pair<D, FMT, false>(p, kvh, a0, a1, kr);
-                f32x4 sc[CS][2];
-    #pragma unroll
-                for (int c = 0; c < CS; ++c) {
-                    u32x4 qr[M::KSTEPS];
-                    qget(c, qr);
-                    pair_scores<D, FMT>(kr, qr, sc[c][0], sc[c][1]);
-                }
-                // keep the V loads after the score MFMAs: K and V of the pair
-                // are never live together, which keeps the path in the
-                // per-sequence path's register budget
-                __builtin_amdgcn_sched_barrier(0);
-                VHalf<D, FMT> vr;
-                issue_v_pair<D, FMT, false>(p, kvh, a0, a1, vr);
-                const int full = t0 + 2 * kBlock;  // every token of the pair is in context
-    #pragma unroll
-                for (int c = 0; c < CS; ++c) {
-                    float x[8], pr[8];
-                    scale_mask(sc[c][0], sc[c][1], p.scale_log2 * kr.s0, p.scale_log2 * kr.s1, t0 + 4 * q, full, true, x);
-                    softmax_update(cst[c], x, pr);
-                    pv_update<D, FMT>(cst[c], vr, pr, t0, full, true, true);
-                }
-            } else {
-    #pragma unroll
-                for (int c = 0; c < CS; ++c) {
-                    float x[8];
-    #pragma unroll
-                    for (int i = 0; i < 8; ++i) x[i] = kNegInf;
-    #pragma unroll
-                    for (int i = 0; i < NS; ++i) {
-                        const int t = i - c * TPG;  // position of sequence i in this column set
-                        if (i < NS && t >= 0 && t < TPG && k < npairs[i]) {
-                            // one sequence's pair at a time (this path is rare:
-                            // register budget over latency)
-                            __builtin_amdgcn_sched_barrier(0);
-                            const bool has1 = 2 * k + 1 < nbp[i];
-                            const int n0 = tile_id(my_id[i], my_hi[i], 2 * k);
-                            const int n1 = has1 ? tile_id(my_id[i], my_hi[i], 2 * k + 1) : n0;
-                            KHalf<D, FMT> kr;
-                            issue_k_pair<D, FMT>(p, kvh, n0, n1, kr);
-                            f32x4 s0v, s1v;
-                            u32x4 qr[M::KSTEPS];
-                            qget(c, qr);
-                            pair_scores<D, FMT>(kr, qr, s0v, s1v);
-                            float xi[8];
-                            scale_mask(s0v, s1v, p.scale_log2 * kr.s0, p.scale_log2 * kr.s1, t0 + 4 * q, ctx[i], has1,
-                                       xi);
-                            if (owner == t) {
-    #pragma unroll
-                                for (int e = 0; e < 8; ++e) x[e] = xi[e];
-                            }
-                        }
-                    }
-                    float pr[8];
-                    softmax_update(cst[c], x, pr);
-    #pragma unroll
-                    for (int i = 0; i < NS; ++i) {
-                        const int t = i - c * TPG;
-                        if (i < NS && t >= 0 && t < TPG && k < npairs[i]) {
-                            __builtin_amdgcn_sched_barrier(0);
-                            const bool has1 = 2 * k + 1 < nbp[i];
-                            const int n0 = tile_id(my_id[i], my_hi[i], 2 * k);
-                            const int n1 = has1 ? tile_id(my_id[i], my_hi[i], 2 * k + 1) : n0;
-                            VHalf<D, FMT> vr;
-                            issue_v_pair<D, FMT>(p, kvh, n0, n1, vr);
-                            pv_update<D, FMT>(cst[c], vr, pr, t0, ctx[i], has1, owner == t);
-                        }
-                    }
-                }
-            }
-        }
     }
 
     // one column set at a time through the workgroup's LDS state
 #pragma unroll
     for (int c = 0; c < CS; ++c) {
         __syncthreads();  // every wave is done with the previous set
-        col_to_lds(cst[c], st, wave);
+        col_to_lds<D, M::kOffset>(cst[c], st, wave);
         __syncthreads();
         merge_waves_store<D, F32OUT>(p, st, 16, part, [&](int cl, int& s, int& qh, int& np) {
             const int i = c * TPG + cl / G;

@@ -87,6 +87,25 @@ __device__ __forceinline__ u32x4 i4x8_to_bf16x8(uint32_t w) {
     return r;
 }
 
+// int4 -> bf16 of the eight nibbles of a dword (low nibble first), offset by
+// +136: flipping a two's-complement nibble's sign bit gives v + 8 in [0, 15],
+// and those four bits OR-ed into the mantissa of bf16 128 (0x4300) make
+// exactly 136 + v. Byte k of the result pairs element 2k (low half) with
+// element 2k + 1 (high half), like i4x8_to_bf16x8.
+__device__ __forceinline__ u32x4 i4x8_to_bf16x8_off136(uint32_t w) {
+    const uint32_t x = w ^ 0x88888888u;
+    const uint32_t a = x & 0x0f0f0f0fu;         // elements 0, 2, 4, 6
+    const uint32_t b = (x >> 4) & 0x0f0f0f0fu;  // elements 1, 3, 5, 7
+    // v_perm_b32: selector bytes 0-3 pick bytes of the second operand (a),
+    // 4-7 bytes of the first (b), 0x0c gives zero
+    u32x4 r;
+    r[0] = __builtin_amdgcn_perm(b, a, 0x0c040c00u) | 0x43004300u;
+    r[1] = __builtin_amdgcn_perm(b, a, 0x0c050c01u) | 0x43004300u;
+    r[2] = __builtin_amdgcn_perm(b, a, 0x0c060c02u) | 0x43004300u;
+    r[3] = __builtin_amdgcn_perm(b, a, 0x0c070c03u) | 0x43004300u;
+    return r;
+}
+
 // Exact int4 -> bf16 of the four nibbles in the low 16 bits.
 __device__ __forceinline__ u32x2 i4x4_to_bf16x4(uint32_t w) {
     u32x4 t = i4x8_to_bf16x8(w);
