@@ -95,15 +95,20 @@ struct Mfma {
         }
     }
 
-    // The decode path takes int4 codes offset by kOff = 136 (two ALU ops per
-    // element instead of an exact widening); the scores subtract kOff * sum(q)
-    // and the accumulator kOff * sum(P), both in fp32.
-    static constexpr bool kOffset = (FMT == FMT_I4);
-    static constexpr float kOff = 136.f;
+    // The decode path takes int8 / int4 codes offset by kOff = 128 / 136 (a
+    // few ALU ops per element instead of an exact signed widening); the
+    // scores subtract kOff * sum(q) and the accumulator kOff * sum(P), both
+    // in fp32.
+    static constexpr bool kOffset = (FMT == FMT_I4 || FMT == FMT_I8);
+    static constexpr float kOff = (FMT == FMT_I4) ? 136.f : 128.f;
 
     __device__ static __forceinline__ u32x4 k_operand_dec(const KRaw& r, int kk) {
-        if constexpr (kOffset) {
+        if constexpr (FMT == FMT_I4) {
             return i4x8_to_bf16x8_off136(r.w[kk]);
+        } else if constexpr (FMT == FMT_I8) {
+            const u32x2 lo = i8x4_to_bf16x4_off128(r.w[2 * kk]);
+            const u32x2 hi = i8x4_to_bf16x4_off128(r.w[2 * kk + 1]);
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
         } else {
             return k_operand(r, kk);
         }
@@ -179,7 +184,7 @@ struct Mfma {
         }
     }
 
-    // bf16 operand (8 tokens) of dim block nb; int4 comes offset by kOff
+    // bf16 operand (8 tokens) of dim block nb; int8 / int4 come offset by kOff
     __device__ static __forceinline__ u32x4 v_pair_op(const VPairRaw& r, int nb) {
         u32x4 a;
         if (FMT == FMT_BF16) {
@@ -187,9 +192,9 @@ struct Mfma {
             a[1] = r.w[4 * nb + 1];
             a[2] = r.w[4 * nb + 2];
             a[3] = r.w[4 * nb + 3];
-        } else if (FMT == FMT_I8) {
-            const u32x2 lo = i8x4_to_bf16x4(r.w[2 * nb]);
-            const u32x2 hi = i8x4_to_bf16x4(r.w[2 * nb + 1]);
+        } else if (FMT == FMT_I8) {  // offset by kOff (see k_operand_dec)
+            const u32x2 lo = i8x4_to_bf16x4_off128(r.w[2 * nb]);
+            const u32x2 hi = i8x4_to_bf16x4_off128(r.w[2 * nb + 1]);
             a[0] = lo[0];
             a[1] = lo[1];
             a[2] = hi[0];

@@ -75,6 +75,22 @@ __device__ __forceinline__ u32x2 i8x4_to_bf16x4(uint32_t w) {
     return r;
 }
 
+// int8 -> bf16 of the four bytes of a dword (byte 0 first), offset by +128:
+// flipping a byte's sign bit gives v + 128 in [0, 255], converted by the
+// unsigned-byte instructions to a float with at most 8 significant bits,
+// whose upper half is then exactly its bf16.
+__device__ __forceinline__ u32x2 i8x4_to_bf16x4_off128(uint32_t w) {
+    const uint32_t x = w ^ 0x80808080u;
+    const uint32_t f0 = __float_as_uint((float)(x & 0xffu));
+    const uint32_t f1 = __float_as_uint((float)((x >> 8) & 0xffu));
+    const uint32_t f2 = __float_as_uint((float)((x >> 16) & 0xffu));
+    const uint32_t f3 = __float_as_uint((float)(x >> 24));
+    u32x2 r;
+    r[0] = __builtin_amdgcn_perm(f1, f0, 0x07060302u);  // high halves of f0 (low) and f1 (high)
+    r[1] = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+    return r;
+}
+
 // Exact int4 -> bf16 of the eight nibbles of a dword (low nibble first).
 __device__ __forceinline__ u32x4 i4x8_to_bf16x8(uint32_t w) {
     u32x4 r;
