@@ -116,10 +116,13 @@ def test_quantized_decode_parity(lib, bits):
 
 @pytest.mark.parametrize("bits", [8, 4])
 def test_workload4_quantized_sampled(lib, bits):
-    c = make_config_case(4, num_seqs=32)
+    """The whole 128 x 8000 batch, in the launch configuration the benchmark
+    times (the partition plan depends on the batch), checked on sampled
+    sequences."""
+    c = make_config_case(4)
     kc, vc, ks, vs = _quant_case(c, bits)
     got = dev_to_f64(gpu_decode(c, kp=kc, vp=vc, kv_bits=bits, k_scales=ks, v_scales=vs))
-    seqs = [0, 7, 31]
+    seqs = [0, 7, 64, 127]
     used = np.unique(c.block_tables[seqs].ravel())
     used = used[used >= 0]
     # oracle quantizes only the blocks those sequences read
