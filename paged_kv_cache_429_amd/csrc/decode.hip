@@ -24,13 +24,14 @@
 // MFMA formulation (bf16 / int8 / int4 KV). Per pair of blocks:
 //   S^T[32 tok x 16 col] = K[tok x d] * Q^T[d x col]   (2 x D/32 MFMA 16x16x32)
 //   O^T[d x col]        += V^T[d x 32 tok] * P^T[32 tok x col] (D/16 MFMA)
-// The 16 columns are the G query heads of the KV head (zero-padded). With
-// the K tile stored in 16-byte chunks of consecutive dims (slot-minor) and
-// the V tile stored transposed, every lane's MFMA operand is a contiguous
-// 16-byte (K) or 8-byte (V) load, and each wave load instruction reads a
-// contiguous 1 KiB (K) or 512 B (V) run. The S^T accumulator layout (lane
-// holds 4 consecutive tokens of one column) is exactly the B-operand layout
-// the P*V product needs, so probabilities never cross lanes.
+// The 16 columns are the G query heads of the KV head (zero-padded). The K
+// tile is stored in 16-byte chunks of consecutive dims (slot-minor), so a
+// lane's K operand is one 16-byte load and a wave's load instruction reads a
+// contiguous 1 KiB. The V tile is stored transposed (a row is the 16 tokens
+// of one dim), and the P.V product's k index gives lane group q the 8
+// consecutive tokens 8 (q % 2) .. + 7 of block q / 2: a lane's V operand is
+// one contiguous half row (16 B for bf16), and the probabilities are
+// regrouped from the S^T accumulator layout by two cross-row lane swaps.
 //
 // fp32 KV uses a plain VALU path with the same decomposition and epilogue.
 #include "pa_attn.h"
@@ -38,7 +39,8 @@
 namespace pa {
 
 // Waves per SIMD the register budget is sized for: the bf16 loop fits three
-// (<= 168 VGPRs); the int8/int4 dequantisation needs more registers.
+// (<= 168 VGPRs); the int4 loop, with two pairs in flight, needs more (int8
+// stays under 168 and runs at three anyway).
 template <int FMT>
 constexpr int decode_waves_per_eu() {
     return FMT == FMT_BF16 ? 3 : 2;
