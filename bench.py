@@ -224,7 +224,8 @@ def prefill_cpu_baseline(c, budget_s):
 def prefill_main(a, torch, B, CONFIGS):
     """Workload 5: the 2048-token causal chunk over 6000 cached tokens alone
     ('5p'), or the whole mixed step ('5': the chunk on one stream and the 64
-    decodes on a second, both bracketed by events on the first)."""
+    decodes concurrently on a second, both bracketed by events on the
+    first)."""
     from synth import make_mixed_case
     pre, dec = make_mixed_case()
     kp = B.alloc_pool(pre.num_blocks, pre.n_kv, pre.d, 16)
@@ -249,10 +250,15 @@ def prefill_main(a, torch, B, CONFIGS):
     torch.cuda.synchronize()
 
     def step():
+        # mixed: the chunk and the decodes of one step run concurrently on two
+        # streams (they only read the pools); a step starts once the previous
+        # one (and the start event on the main stream) is done, and the main
+        # stream joins the decode stream before the step's end
+        if mixed:
+            s_dec.wait_stream(s_main)
         B.prefill_chunk(qp, cu, kp, vp, tp, cp, n_kv_heads=pre.n_kv, max_q_len=pre.max_q_len,
                         max_context_len=pre.max_context_len, out=op, stream=s_main)
         if mixed:
-            s_dec.wait_stream(s_main)
             B.decode(qd, kp, vp, td, cd, n_kv_heads=dec.n_kv, max_context_len=dec.max_context_len, out=od,
                      workspace=ws, stream=s_dec)
             s_main.wait_stream(s_dec)
