@@ -281,6 +281,17 @@ __device__ __forceinline__ void pair_scores(const KHalf<D, FMT>& r, const u32x4*
 __device__ __forceinline__ void scale_mask(const f32x4& s0, const f32x4& s1, float c0, float c1, int tok0, int ctx,
                                            bool has1, float* x) {
     const int tok1 = tok0 + kBlock;
+    // a pair wholly in context (the usual case; the test is wave-uniform,
+    // as tok0 - 4q is) needs no select
+    const int t0 = tok0 - 4 * ((threadIdx.x & 63) >> 4);
+    if (has1 && t0 + 2 * kBlock <= ctx) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = s0[i] * c0;
+            x[4 + i] = s1[i] * c1;
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         x[i] = (tok0 + i < ctx) ? s0[i] * c0 : kNegInf;
@@ -311,8 +322,12 @@ __device__ __forceinline__ void softmax_update(ColState<D>& c, const float* x, f
     }
     c.l = c.l * alpha + psum;
     c.corr *= alpha;
+    // alpha is exactly 1 in every column of the wave unless some maximum
+    // moved; multiplying by 1 changes nothing, so that common case skips it
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb) c.acc[nb] *= alpha;
+        for (int nb = 0; nb < D / 16; ++nb) c.acc[nb] *= alpha;
+    }
 }
 
 // O^T += V^T P^T for one pair. The k index of the product runs over the
