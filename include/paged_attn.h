@@ -139,7 +139,8 @@ uint64_t pa_kv_cache_bytes(int n_layers, int n_kv_heads, int d_head, int kv_bits
  *              counters must be zero before the first call that uses the
  *              workspace (allocate it zero-filled); every call that completes
  *              leaves them zero again. The rest holds the partials of split
- *              sequences and needs no initialisation. One workspace serves
+ *              sequences and of the prefix pass, and the prefix pass's
+ *              per-tile runs; it needs no initialisation. One workspace serves
  *              calls of any shape, but calls that share it must be ordered
  *              (same stream, or synchronised): overlapping calls race.
  * partition_blocks  blocks per context partition pb (even, 2..64), or 0 to
@@ -147,15 +148,32 @@ uint64_t pa_kv_cache_bytes(int n_layers, int n_kv_heads, int d_head, int kv_bits
  *              partitions processed in parallel and merged by log-sum-exp
  *              within the same launch: the last partition of a (sequence,
  *              KV head) to finish merges them, in partition order. Partition
- *              p starts at block p * pb; the last one also takes a remainder
- *              of up to pb / 4 blocks. The split depends only on the
- *              arguments' values on the host and on each sequence's length,
- *              never on physical block ids.
- *              Consecutive sequences (16 / G of them, for G = 4 or 8) whose
- *              tables name the same physical blocks for a partition's first
- *              two blocks are processed together, each shared block being
- *              read once for the group; results are bit-identical to those
- *              of private copies of the same blocks.
+ *              p starts at block b0 + p * pb; the last one also takes a
+ *              remainder of up to pb / 4 blocks. b0 is 0 unless the prefix
+ *              pass below took a run of the sequence's first blocks (then
+ *              b0 is the run's length). The split depends only on the
+ *              arguments' values on the host, each sequence's length and
+ *              that run.
+ *              Shared prefixes ([JE] "Prefix caching"), two mechanisms:
+ *              - Prefix pass. When the batch has at least 512 query rows
+ *                per KV head (num_seqs * G >= 512) with bf16 pools, d_head
+ *                128 and G dividing 32, a first launch takes tiles of
+ *                256 / G consecutive sequences. In each, the longest
+ *                leading run of blocks that every member holds at the same
+ *                physical ids and that ends before every member's last
+ *                token, cut to a multiple of 4 blocks, is attended, if it
+ *                holds at least 16 blocks, for all the tile's query rows at
+ *                once (one MFMA contraction, each shared block read once
+ *                per tile and KV head); its log-sum-exp partials are merged
+ *                with the decode's partitions of the blocks after the run.
+ *                Such sequences agree with private copies of the same
+ *                blocks to rounding, not bit for bit.
+ *              - Shared workgroups. Elsewhere, consecutive sequences (16 / G
+ *                of them, for G = 4 or 8) whose tables name the same
+ *                physical blocks for a partition's first two blocks are
+ *                processed together, each shared block being read once for
+ *                the group; results are bit-identical to those of private
+ *                copies of the same blocks.
  * ------------------------------------------------------------------------ */
 size_t paged_attn_decode_workspace_size(int num_seqs, int n_heads, int n_kv_heads, int d_head,
                                         int max_context_len, int partition_blocks);

@@ -53,6 +53,25 @@ int plan_partition_blocks(int num_seqs, int n_kv, int max_context_len, int reque
     return pb;
 }
 
+// Prefix partitions per tile (0: no prefix pass) for a decode of this shape.
+// The pass runs for d_head 128 and G dividing 32 (one 32-row MFMA tile per
+// wave) when the batch has at least two tiles' worth of query rows per KV
+// head and the longest context leaves room for a run of kMinPrefixBlocks;
+// the run is split so that the pass has about one workgroup per compute
+// unit, each range holding at least kMinPrefixBlocks blocks. The element
+// format is checked by the caller (bf16 pools only).
+int plan_prefix_parts(int num_seqs, int n_heads, int n_kv, int d, int ctx_cap, int pmax) {
+    const int G = n_heads / n_kv;
+    if (d != 128 || G <= 0 || 32 % G != 0 || pmax <= 1) return 0;
+    if ((long)num_seqs * G < 2L * pa::kPrefixRows) return 0;
+    const int max_run = (ctx_cap - 1) / PA_BLOCK_SIZE;
+    if (max_run < pa::kMinPrefixBlocks) return 0;
+    const int ts = pa::kPrefixRows / G;
+    const long tiles = ((long)num_seqs + ts - 1) / ts;
+    const long want = ((long)cu_count() + tiles * n_kv - 1) / (tiles * n_kv);
+    return (int)std::max(1L, std::min(want, (long)(max_run / pa::kMinPrefixBlocks)));
+}
+
 bool valid_common(int num_seqs, int num_blocks, int block_size, int n_heads, int n_kv_heads, int d_head) {
     if (num_seqs < 0 || num_blocks <= 0 || n_heads <= 0 || n_kv_heads <= 0 || d_head <= 0) return false;
     if (block_size != PA_BLOCK_SIZE) return false;
@@ -97,9 +116,11 @@ size_t paged_attn_decode_workspace_size(int num_seqs, int n_heads, int n_kv_head
                                         int max_context_len, int partition_blocks) {
     if (num_seqs <= 0 || n_heads <= 0 || n_kv_heads <= 0 || d_head <= 0 || max_context_len <= 0) return 0;
     if (partition_blocks < 0 || partition_blocks > 64 || (partition_blocks & 1)) return 0;
+    if (n_heads % n_kv_heads != 0) return 0;
     const int pb = plan_partition_blocks(num_seqs, n_kv_heads, max_context_len, partition_blocks);
     const int pmax = pa::num_parts(ceil_div(max_context_len, PA_BLOCK_SIZE), pb);
-    return pa::decode_workspace_bytes(num_seqs, n_heads, n_kv_heads, d_head, pmax);
+    const int kpmax = plan_prefix_parts(num_seqs, n_heads, n_kv_heads, d_head, max_context_len, pmax);
+    return pa::decode_workspace_bytes(num_seqs, n_heads, n_kv_heads, d_head, pmax, kpmax);
 }
 
 int paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
@@ -160,14 +181,45 @@ int paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
             if (p.n_shared == 0) p.share_n = 0;
         }
     }
-    const size_t need = pa::decode_workspace_bytes(num_seqs, n_heads, n_kv_heads, d_head, p.pmax);
+    // Prefix pass (bf16 pools): a launch before the decode that attends each
+    // tile's common leading run of blocks for all its rows at once.
+    p.kpmax = fmt == 1 ? plan_prefix_parts(num_seqs, n_heads, n_kv_heads, d_head, p.ctx_cap, p.pmax) : 0;
+    p.pslots = p.pmax + p.kpmax;
+    p.prefix_ts = p.kpmax > 0 ? pa::kPrefixRows / G : 0;
+    const size_t need = pa::decode_workspace_bytes(num_seqs, n_heads, n_kv_heads, d_head, p.pmax, p.kpmax);
+    int* plan = nullptr;
     if (need > 0) {
         if ((long)num_seqs * n_kv_heads > pa::kMaxCounterPairs) return PA_ERR_UNSUPPORTED;
         if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
-        pa::decode_workspace_carve(workspace, num_seqs, n_heads, n_kv_heads, d_head, p.pmax, &p.part_acc, &p.part_ml,
-                                   &p.counters);
+        pa::decode_workspace_carve(workspace, num_seqs, n_heads, n_kv_heads, d_head, p.pmax, p.kpmax, &p.part_acc,
+                                   &p.part_ml, &p.counters, &plan);
     }
-    const hipError_t e = pa::launch_decode(p, d_head, fmt, static_cast<hipStream_t>(stream));
+    p.plan = plan;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p.kpmax > 0) {
+        pa::PrefillParams pp{};
+        pp.q = q;
+        pp.k_pool = k_pool;
+        pp.v_pool = v_pool;
+        pp.tables = block_tables;
+        pp.ctx = context_lens;
+        pp.max_blocks = max_blocks_per_seq;
+        pp.ctx_cap = p.ctx_cap;
+        pp.num_seqs = num_seqs;
+        pp.num_blocks = num_blocks;
+        pp.n_heads = n_heads;
+        pp.n_kv = n_kv_heads;
+        pp.group = G;
+        pp.scale_log2 = p.scale_log2;
+        pp.part_acc = p.part_acc;
+        pp.part_ml = p.part_ml;
+        pp.plan = plan;
+        pp.pslots = p.pslots;
+        pp.kpmax = p.kpmax;
+        const hipError_t e = pa::launch_prefix(pp, st);
+        if (e != hipSuccess) return PA_ERR_HIP;
+    }
+    const hipError_t e = pa::launch_decode(p, d_head, fmt, st);
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

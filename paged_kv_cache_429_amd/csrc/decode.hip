@@ -74,9 +74,17 @@ void decode_kernel(DecodeParams p) {
     // Highest partitions first, partition 0 of every sequence last: the
     // last round of workgroups then holds whole short sequences and full
     // first partitions, of similar size, instead of a random mix (the
-    // order changes nothing but when a unit runs).
-    u.s = rest % p.num_seqs;
-    u.part = p.pmax - 1 - rest / p.num_seqs;
+    // order changes nothing but when a unit runs). With the prefix pass a
+    // sequence's partitions are consecutive instead, so that the units left
+    // without blocks (the run shortened the sequence) are spread over the
+    // launch rather than bunched at its start.
+    if (p.prefix_ts > 0) {
+        u.s = rest / p.pmax;
+        u.part = rest % p.pmax;
+    } else {
+        u.s = rest % p.num_seqs;
+        u.part = p.pmax - 1 - rest / p.num_seqs;
+    }
     u.ctx = min(p.ctx[u.s], p.ctx_cap);
     if (u.ctx <= 0) {
         if (u.part == 0) {
@@ -86,11 +94,14 @@ void decode_kernel(DecodeParams p) {
         return;
     }
     u.nblk = (u.ctx + kBlock - 1) / kBlock;
-    u.nparts = num_parts(u.nblk, p.pb);
+    // blocks [0, run) were attended by the prefix pass (run < nblk)
+    const int run = p.prefix_ts > 0 ? p.plan[u.s / p.prefix_ts] : 0;
+    u.slot0 = prefix_parts(run, p.kpmax);
+    u.nparts = num_parts(u.nblk - run, p.pb);
     if (u.part >= u.nparts) return;
-    u.b_begin = u.part * p.pb;
-    u.b_end = part_end(u.nblk, p.pb, u.part, u.nparts);
-    if (p.share_n > 0) {  // taken by a shared-prefix workgroup?
+    u.b_begin = run + u.part * p.pb;
+    u.b_end = run + part_end(u.nblk - run, p.pb, u.part, u.nparts);
+    if (p.share_n > 0 && run == 0) {  // taken by a shared-prefix workgroup?
         const int grp = u.s / p.share_n;
         if ((grp + 1) * p.share_n <= p.num_seqs && group_shares(p, grp * p.share_n, u.part)) return;
     }
@@ -117,23 +128,28 @@ void decode_kernel(DecodeParams p) {
 // counters stay zero between calls and partial data never lands on them.
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t decode_workspace_bytes(int num_seqs, int n_heads, int n_kv, int d, int pmax) {
+// The prefix pass adds kpmax partial slots per (sequence, query head) and
+// one plan entry per tile (num_seqs entries bound the tile count).
+size_t decode_workspace_bytes(int num_seqs, int n_heads, int n_kv, int d, int pmax, int kpmax) {
     (void)n_kv;
     if (pmax <= 1) return 0;
-    const size_t rows = (size_t)num_seqs * n_heads * pmax;
-    return kCounterBytes + align256(rows * d * sizeof(float)) + align256(rows * 2 * sizeof(float));
+    const size_t rows = (size_t)num_seqs * n_heads * (pmax + kpmax);
+    const size_t plan = kpmax > 0 ? align256((size_t)num_seqs * sizeof(int)) : 0;
+    return kCounterBytes + align256(rows * d * sizeof(float)) + align256(rows * 2 * sizeof(float)) + plan;
 }
 
-void decode_workspace_carve(void* ws, int num_seqs, int n_heads, int n_kv, int d, int pmax, float** part_acc,
-                            float** part_ml, int** counters) {
+void decode_workspace_carve(void* ws, int num_seqs, int n_heads, int n_kv, int d, int pmax, int kpmax,
+                            float** part_acc, float** part_ml, int** counters, int** plan) {
     (void)n_kv;
-    const size_t rows = (size_t)num_seqs * n_heads * pmax;
+    const size_t rows = (size_t)num_seqs * n_heads * (pmax + kpmax);
     char* b = static_cast<char*>(ws);
     *counters = reinterpret_cast<int*>(b);
     b += kCounterBytes;
     *part_acc = reinterpret_cast<float*>(b);
     b += align256(rows * d * sizeof(float));
     *part_ml = reinterpret_cast<float*>(b);
+    b += align256(rows * 2 * sizeof(float));
+    *plan = kpmax > 0 ? reinterpret_cast<int*>(b) : nullptr;
 }
 
 template <int D, int FMT>

@@ -28,8 +28,10 @@ struct WaveState {
     float acc[kWaves][16][D + 4];
 };
 
+// slot0: partial slots before this unit's partitions (the prefix pass's);
+// partition `part` stores its partial in slot slot0 + part.
 struct Unit {
-    int s, kvh, part, ctx, nblk, nparts, b_begin, b_end;
+    int s, kvh, part, ctx, nblk, nparts, b_begin, b_end, slot0;
 };
 
 // Physical id of block j (wave-uniform, 0 <= j < 128) of a partition whose
@@ -871,7 +873,7 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& p, int s, int
         float* lsum = lw + 2 * G * np;  // [G] total weighted sum
         for (int t = tid; t < G * np; t += NT) {
             const int g = t / np, q = t - g * np;
-            const float* ml = p.part_ml + ((h0 + g) * p.pmax + q) * 2;
+            const float* ml = p.part_ml + ((h0 + g) * p.pslots + q) * 2;
             const float mv = load_agent(ml);
             const float lv = load_agent(ml + 1);
             lm[t] = mv;
@@ -903,7 +905,7 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& p, int s, int
 #pragma unroll
                     for (int c = 0; c < kChunk; ++c) {
                         a[j][c] = (idx < G * D && q0 + c < np)
-                                      ? load_agent(p.part_acc + ((h0 + g) * p.pmax + q0 + c) * D + d)
+                                      ? load_agent(p.part_acc + ((h0 + g) * p.pslots + q0 + c) * D + d)
                                       : 0.f;
                     }
                 }
@@ -929,8 +931,8 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& p, int s, int
     // (M, L, O) rescaled when a later chunk raises the maximum
     for (int idx = tid; idx < G * D; idx += NT) {
         const int g = idx / D, d = idx - g * D;
-        const float* ml = p.part_ml + (h0 + g) * p.pmax * 2;
-        const float* acc = p.part_acc + (h0 + g) * p.pmax * D + d;
+        const float* ml = p.part_ml + (h0 + g) * p.pslots * 2;
+        const float* acc = p.part_acc + (h0 + g) * p.pslots * D + d;
         float M = kNegInf, L = 0.f, O = 0.f;
         for (int p0 = 0; p0 < np; p0 += kChunk) {
             float mv[kChunk], lv[kChunk], av[kChunk];
@@ -961,11 +963,11 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& p, int s, int
 
 // Merge the waves' column states held in LDS (in wave order) for columns
 // 0..ncols-1 and store each column's result: the output row of a sequence
-// with one partition, else this partition's partial (max, sum,
-// unnormalised accumulator). info(col, s, qh, nparts) names the column's
-// sequence, query head and partition count.
+// with one partial in all, else the partial (max, sum, unnormalised
+// accumulator) in slot `slot`. info(col, s, qh, nparts) names the column's
+// sequence, query head and number of partials.
 template <int D, bool F32OUT, typename Info>
-__device__ __forceinline__ void merge_waves_store(const DecodeParams& p, const WaveState<D>& st, int ncols, int part,
+__device__ __forceinline__ void merge_waves_store(const DecodeParams& p, const WaveState<D>& st, int ncols, int slot,
                                                   Info info) {
     for (int idx = threadIdx.x; idx < ncols * D; idx += kThreads) {
         const int col = idx / D, d = idx - col * D;
@@ -985,13 +987,64 @@ __device__ __forceinline__ void merge_waves_store(const DecodeParams& p, const W
         if (nparts == 1) {
             store_out<D, F32OUT>(p, h * D + d, O / L);
         } else {
-            const size_t row = h * p.pmax + part;
+            const size_t row = h * p.pslots + slot;
             store_agent(p.part_acc + row * D + d, O);
             if (d == 0) {
                 store_agent(p.part_ml + row * 2, M);
                 store_agent(p.part_ml + row * 2 + 1, L);
             }
         }
+    }
+}
+
+// Merge the waves' column states in LDS with the np prefix-pass partials of
+// the same rows (slots 0..np-1, written by an earlier launch) and store the
+// outputs: the path of a unit that is the only decode partition of its
+// sequence, which needs no partial of its own.
+template <int D, bool F32OUT>
+__device__ __forceinline__ void merge_waves_prefix_store(const DecodeParams& p, const Unit& u, const WaveState<D>& st,
+                                                         int np) {
+    constexpr int kChunk = 4;
+    const int G = p.group;
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+        const int col = idx / D, d = idx - col * D;
+        const size_t h = (size_t)u.s * p.n_heads + u.kvh * G + col;
+        float M = st.m[0][col];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, st.m[w][col]);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float e = __builtin_amdgcn_exp2f(st.m[w][col] - M);  // 0 for a wave without blocks
+            L += e * st.l[w][col];
+            O += e * st.acc[w][col][d];
+        }
+        const float* ml = p.part_ml + h * p.pslots * 2;
+        const float* acc = p.part_acc + h * p.pslots * D + d;
+        for (int q0 = 0; q0 < np; q0 += kChunk) {
+            float mv[kChunk], lv[kChunk], av[kChunk];
+#pragma unroll
+            for (int c = 0; c < kChunk; ++c) {
+                const bool ok = q0 + c < np;
+                mv[c] = ok ? load_agent(ml + 2 * (q0 + c)) : kNegInf;
+                lv[c] = ok ? load_agent(ml + 2 * (q0 + c) + 1) : 0.f;
+                av[c] = ok ? load_agent(acc + (size_t)(q0 + c) * D) : 0.f;
+            }
+            float Mc = M;
+#pragma unroll
+            for (int c = 0; c < kChunk; ++c) Mc = fmaxf(Mc, mv[c]);
+            const float r = __builtin_amdgcn_exp2f(M - Mc);
+            L *= r;
+            O *= r;
+#pragma unroll
+            for (int c = 0; c < kChunk; ++c) {
+                const float e = __builtin_amdgcn_exp2f(mv[c] - Mc);  // 0 for padding (m = -inf)
+                L += e * lv[c];
+                O += e * av[c];
+            }
+            M = Mc;
+        }
+        store_out<D, F32OUT>(p, h * D + d, O / L);
     }
 }
 
@@ -1009,29 +1062,35 @@ __device__ __forceinline__ bool arrive(const DecodeParams& p, int s, int kvh, in
 
 // Epilogue of a (sequence, KV head, partition) workgroup: merge the waves,
 // store, and if this was the last partition of a split sequence to arrive,
-// merge all its partials.
+// merge all its partials (the prefix pass's first, written by an earlier
+// launch, so only this launch's partitions are counted).
 // merge_scratch: `cap` floats of LDS, which may alias st.
 template <int D, bool F32OUT>
 __device__ __forceinline__ void epilogue(const DecodeParams& p, const Unit& u, WaveState<D>& st,
                                          float* merge_scratch, int cap) {
     __syncthreads();
     const int G = p.group;
-    merge_waves_store<D, F32OUT>(p, st, G, u.part, [&](int col, int& s, int& qh, int& np) {
+    const int ntotal = u.slot0 + u.nparts;
+    if (u.nparts == 1 && u.slot0 > 0) {
+        merge_waves_prefix_store<D, F32OUT>(p, u, st, u.slot0);
+        return;
+    }
+    merge_waves_store<D, F32OUT>(p, st, G, u.slot0 + u.part, [&](int col, int& s, int& qh, int& np) {
         s = u.s;
         qh = u.kvh * G + col;
-        np = u.nparts;
+        np = ntotal;
     });
-    if (u.nparts == 1) return;
+    if (ntotal == 1) return;
 
     __shared__ int last;
     // Every thread's partial stores have reached the coherence point before
-    // the workgroup's arrival is counted.
+    // the workgroup's arrival is counted (or, alone, before it merges).
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) last = arrive(p, u.s, u.kvh, u.nparts);
     __syncthreads();
     if (!last) return;
-    merge_partials<D, F32OUT, kThreads>(p, u.s, u.kvh, u.nparts, merge_scratch, cap, threadIdx.x);
+    merge_partials<D, F32OUT, kThreads>(p, u.s, u.kvh, ntotal, merge_scratch, cap, threadIdx.x);
 }
 
 // -----------------------------------------------------------------------------
@@ -1094,6 +1153,9 @@ __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, Wav
     const int part = rest % p.pmax;
     const int grp = rest / p.pmax;
     const int s0 = grp * NS;
+    // a tile whose common run the prefix pass took is planned from the run
+    // on, by the per-sequence workgroups alone
+    if (p.prefix_ts > 0 && p.plan[s0 / p.prefix_ts] > 0) return;
     if (!group_shares(p, s0, part)) return;
 
     const int G = p.group;

@@ -26,6 +26,27 @@ __host__ __device__ inline int part_end(int nblk, int pb, int part, int nparts) 
     return part + 1 == nparts ? nblk : (part + 1) * pb;
 }
 
+// Prefix pass ("jovanaeducation" guide a2-inf-2, section "Prefix caching";
+// "KV cache, GQA, paging and continuous batching", section
+// "PagedAttention..."): the batch is cut into tiles of kPrefixRows / G
+// consecutive sequences (kPrefixRows query rows per KV head). For each tile,
+// the longest leading run of logical blocks that every member holds at the
+// same physical ids, with at least one token of every member after it, is
+// found and cut to whole key stages of kPrefixStageBlocks blocks (a masked
+// partial stage would cost the pass more registers than the few blocks
+// save); a run of kMinPrefixBlocks or more is attended by one MFMA
+// contraction over all the tile's rows (bf16 pools, d_head 128), its
+// stages split into prefix_parts() near-equal ranges that each leave a
+// log-sum-exp partial. The decode workgroups then cover only the blocks
+// after the run and merge with those partials.
+constexpr int kPrefixRows = 256;
+constexpr int kPrefixStageBlocks = 4;
+constexpr int kMinPrefixBlocks = 16;
+__host__ __device__ inline int prefix_parts(int run_blocks, int kpmax) {
+    const int stages = run_blocks / kPrefixStageBlocks;
+    return stages < kpmax ? stages : kpmax;
+}
+
 struct DecodeParams {
     const void* q;
     const void* k_pool;
@@ -35,8 +56,8 @@ struct DecodeParams {
     const int32_t* tables;
     const int32_t* ctx;
     void* out;
-    float* part_acc;    // [num_seqs][n_heads][pmax][d]   (unnormalised)
-    float* part_ml;     // [num_seqs][n_heads][pmax][2]   (max, sum) in log2 units
+    float* part_acc;    // [num_seqs][n_heads][pslots][d]   (unnormalised)
+    float* part_ml;     // [num_seqs][n_heads][pslots][2]   (max, sum) in log2 units
     int* counters;      // [num_seqs][n_kv] partitions arrived (zero between calls)
     int max_blocks;     // table row stride
     int ctx_cap;        // min(max_context_len, 16 * max_blocks)
@@ -50,6 +71,10 @@ struct DecodeParams {
     float scale_log2;   // log2(e) / sqrt(d)
     int share_n;        // sequences per shared-prefix group (0: no shared-prefix workgroups)
     int n_shared;       // shared-prefix workgroups, first in the grid: (S / share_n) * pmax * n_kv
+    int pslots;         // partial slots per (sequence, query head): kpmax + pmax
+    int prefix_ts;      // sequences per prefix-pass tile (0: no prefix pass)
+    int kpmax;          // prefix partitions per tile at most
+    const int* plan;    // [tiles] run (blocks) the prefix pass covered, written by it
 };
 
 // Bytes of the arrival-counter region at the start of a decode workspace:
@@ -59,9 +84,9 @@ constexpr long kMaxCounterPairs = (long)(kCounterBytes / sizeof(int));
 
 // Workspace bytes for the arrival counters and split-context partials (0
 // when pmax == 1).
-size_t decode_workspace_bytes(int num_seqs, int n_heads, int n_kv, int d, int pmax);
-void decode_workspace_carve(void* ws, int num_seqs, int n_heads, int n_kv, int d, int pmax, float** part_acc,
-                            float** part_ml, int** counters);
+size_t decode_workspace_bytes(int num_seqs, int n_heads, int n_kv, int d, int pmax, int kpmax);
+void decode_workspace_carve(void* ws, int num_seqs, int n_heads, int n_kv, int d, int pmax, int kpmax,
+                            float** part_acc, float** part_ml, int** counters, int** plan);
 
 // fmt: 0 fp32, 1 bf16, 2 int8, 3 int4. Launches the decode kernel on
 // `stream`.
@@ -86,9 +111,20 @@ struct PrefillParams {
     int group;
     int max_q_len;
     float scale_log2;
+    // prefix pass only (see kPrefixRows)
+    float* part_acc;
+    float* part_ml;
+    int* plan;
+    int pslots;
+    int kpmax;
 };
 
 hipError_t launch_prefill(const PrefillParams& p, int d, int fmt, hipStream_t stream);
+
+// The prefix pass of a decode step (bf16 pools, d_head 128, 32 % G == 0):
+// num_seqs, tables, ctx, ctx_cap, q as for the decode; writes the tiles'
+// plan entries and the prefix partials in slots 0 .. prefix_parts() - 1.
+hipError_t launch_prefix(const PrefillParams& p, hipStream_t stream);
 
 hipError_t launch_quantize(const void* src, void* codes, uint16_t* scales, const int32_t* block_ids, int n_ids,
                            int num_blocks, int n_kv, int d, int bits, int kind, hipStream_t stream);

@@ -269,6 +269,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p, int 
 // The S^T accumulator of a lane is exactly its P^T operand (keys
 // 8*(r/4) + 4*(l/32) + r%4 of its column), and the V^T operand reads the
 // same keys as one 16-byte run from the staged V layout.
+//
+// PREFIX: the prefix pass of a decode step. The rows are those of 256/G
+// consecutive decode sequences (a tile) instead of chunk tokens, the keys a
+// range of the tile's common leading run of blocks (whole stages), which
+// every row sees whole (no mask). Every workgroup of the tile first finds
+// that run (the same way, so they agree); the result is a log-sum-exp
+// partial per row.
 // -----------------------------------------------------------------------------
 constexpr int kTileWaves = 8;
 constexpr int kTileThreads = kTileWaves * kWave;
@@ -277,24 +284,75 @@ constexpr int kStageKeys = kStageBlocks * kBlock;   // 64
 constexpr int kTile128 = kBlock * 128 * 2;          // 4 KiB
 constexpr int kStageBytes = 2 * kStageBlocks * kTile128;
 
+// Longest leading run of blocks that the n (>= 2) sequences from s0 on all
+// hold at the same physical ids, ending at least one token before the end
+// of the shortest of them; 0 if n < 2. Whole workgroup; every thread gets
+// the result. Blocks are compared in windows of 256 from the start, so a
+// batch without a common prefix costs one window.
+__device__ __forceinline__ int common_run(const PrefillParams& p, int s0, int n, int* red) {
+    const int tid = threadIdx.x;
+    if (tid == 0) *red = 0x7fffffff;
+    __syncthreads();
+    int cap = 0x7fffffff;
+    for (int i = tid; i < n; i += kTileThreads) {
+        const int c = min(p.ctx[s0 + i], p.ctx_cap);
+        cap = min(cap, c > 0 ? (c - 1) / kBlock : -1);  // whole blocks before the last token
+    }
+    atomicMin(red, cap);
+    __syncthreads();
+    int run = n >= 2 ? max(*red, 0) : 0;
+    const int32_t* t0 = p.tables + (size_t)s0 * p.max_blocks;
+    for (int j0 = 0; j0 < run; j0 += 256) {
+        const int w = min(256, run - j0);
+        __syncthreads();  // every thread has read *red
+        if (tid == 0) *red = 0x7fffffff;
+        __syncthreads();
+        int miss = 0x7fffffff;
+        for (int e = tid; e < (n - 1) * w; e += kTileThreads) {
+            const int i = 1 + e / w;
+            const int j = j0 + (e - (i - 1) * w);
+            if (p.tables[(size_t)(s0 + i) * p.max_blocks + j] != t0[j]) miss = min(miss, j);
+        }
+        atomicMin(red, miss);
+        __syncthreads();
+        if (*red != 0x7fffffff) run = *red;  // uniform: ends the loop
+    }
+    return run;
+}
+
+template <bool PREFIX>
 __global__ __launch_bounds__(kTileThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_tile_kernel(PrefillParams p, int ntile) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
     constexpr int D = 128;
     const int G = p.group;
-    const int TPW = 32 / G;  // chunk tokens per wave
+    const int TPW = 32 / G;  // chunk tokens (prefix: sequences) per wave
     const int QT = kTileWaves * TPW;
     const int unit = blockIdx.x;
     const int kvh = unit % p.n_kv;
     const int rest = unit / p.n_kv;
-    const int qt = rest % ntile;
-    const int s = rest / ntile;
-    const int q0 = p.cu_q_lens[s];
-    const int qlen = p.cu_q_lens[s + 1] - q0;
-    const int i0 = qt * QT;
-    if (i0 >= qlen) return;
-    const int ctx = min(p.ctx[s], p.ctx_cap);
-    const int shift = ctx - qlen;  // absolute position of chunk row 0
+    // chunk: rows i0.. of sequence s (query rows q0 + i); prefix: sequences
+    // i0.. (query rows i), keys of stages [st_begin, st_end)
+    int s, q0, qlen, i0, ctx, shift, st_begin = 0, st_end = 0, kp = 0, tile = 0;
+    if constexpr (PREFIX) {
+        kp = rest % p.kpmax;
+        tile = rest / p.kpmax;
+        s = tile * QT;  // the tile's first sequence, whose table row is read
+        q0 = 0;
+        qlen = p.num_seqs;
+        i0 = s;
+        ctx = 0x3fffffff;  // every key of the run is in every row's context
+        shift = 0x3fffffff;
+    } else {
+        const int qt = rest % ntile;
+        s = rest / ntile;
+        q0 = p.cu_q_lens[s];
+        qlen = p.cu_q_lens[s + 1] - q0;
+        i0 = qt * QT;
+        if (i0 >= qlen) return;
+        ctx = min(p.ctx[s], p.ctx_cap);
+        shift = ctx - qlen;  // absolute position of chunk row 0
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -315,12 +373,31 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
             qop[kk] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * kk + 8 * half) : u32x4{0u, 0u, 0u, 0u};
         }
     }
-    const int i_last = min(qlen, i0 + QT) - 1;
-    const int kend = shift + i_last + 1;  // keys [0, kend) are visible to some row
+    if constexpr (PREFIX) {  // the tile's run and this workgroup's range of it (Q loads in flight)
+        __shared__ int red;
+        int run = common_run(p, s, min(QT, p.num_seqs - s), &red);
+        run -= run % kPrefixStageBlocks;
+        if (run < kMinPrefixBlocks) run = 0;
+        if (kp == 0 && kvh == 0 && tid == 0) p.plan[tile] = run;
+        const int nparts = prefix_parts(run, p.kpmax);
+        if (kp >= nparts) return;
+        const int stages = run / kPrefixStageBlocks;
+        st_begin = kp * stages / nparts;
+        st_end = (kp + 1) * stages / nparts;
+    }
     const int wfirst = i0 + wave * TPW;
-    const int wave_kmax = wfirst < qlen ? shift + min(qlen - 1, wfirst + TPW - 1) : -1;
-    const int nblk = (kend + kBlock - 1) / kBlock;
-    const int nstage = (kend + kStageKeys - 1) / kStageKeys;
+    int wave_kmax = 0, nblk, nstage;
+    if constexpr (PREFIX) {
+        nblk = st_end * kStageBlocks;
+        nstage = st_end;
+    } else {
+        const int i_last = min(qlen, i0 + QT) - 1;
+        const int kend = shift + i_last + 1;  // keys [0, kend) are visible to some row
+        wave_kmax = wfirst < qlen ? shift + min(qlen - 1, wfirst + TPW - 1) : -1;
+        nblk = (kend + kBlock - 1) / kBlock;
+        nstage = (kend + kStageKeys - 1) / kStageKeys;
+        st_end = nstage;
+    }
 
     const int32_t* trow = p.tables + (size_t)s * p.max_blocks;
     const uint8_t* kpool = reinterpret_cast<const uint8_t*>(p.k_pool);
@@ -485,11 +562,11 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
         __builtin_amdgcn_s_setprio(0);
     };
 
-    prefetch(0, lds);
-    commit(0, lds);
+    prefetch(st_begin, lds + (st_begin & 1) * kStageBytes);
+    commit(st_begin, lds + (st_begin & 1) * kStageBytes);
     __builtin_amdgcn_s_waitcnt(0);  // this thread's K loads have landed
     __syncthreads();
-    for (int st = 0; st < nstage; ++st) {
+    for (int st = st_begin; st < nstage; ++st) {
         uint8_t* buf = lds + (st & 1) * kStageBytes;
         uint8_t* nbuf = lds + ((st + 1) & 1) * kStageBytes;
         // the other buffer was last read before the previous barrier
@@ -498,7 +575,7 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
         // Rows of this wave whose position is at least kb + 63 see the whole
         // stage; only a stage on the causal diagonal needs the mask. (Rows
         // past the chunk end never get stored.)
-        if (kb + kStageKeys - 1 <= shift + wfirst) {
+        if (PREFIX || kb + kStageKeys - 1 <= shift + wfirst) {
             stage(buf, kb, std::false_type{});
         } else if (kb <= wave_kmax) {
             stage(buf, kb, std::true_type{});
@@ -512,6 +589,22 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
 
     const float lt = l + __shfl_xor(l, 32);
     if (!row_ok) return;
+    if constexpr (PREFIX) {
+        // partial of the row in slot kp: (max, sum) in log2 units and the
+        // unnormalised accumulator
+        const size_t row = ((size_t)i * H + kvh * G + n % G) * p.pslots + kp;
+        float* arow = p.part_acc + row * D;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const f32x4 o = {acc[dt][4 * rr + 0], acc[dt][4 * rr + 1], acc[dt][4 * rr + 2], acc[dt][4 * rr + 3]};
+                *reinterpret_cast<f32x4*>(arow + 32 * dt + 8 * rr + 4 * half) = o;
+            }
+        }
+        if (half == 0) *reinterpret_cast<f32x2*>(p.part_ml + row * 2) = f32x2{m, lt};
+        return;
+    }
     const float inv = 1.f / lt;
     uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + ((size_t)(q0 + i) * H + kvh * G + n % G) * D;
 #pragma unroll
@@ -553,12 +646,14 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(PrefillParams pp)
     p.n_kv = pp.n_kv;
     p.group = pp.group;
     p.pmax = 1;
+    p.pslots = 1;
     p.scale_log2 = pp.scale_log2;
 
     Unit u;
     u.s = q0 + i;  // output / query row
     u.kvh = kvh;
     u.part = 0;
+    u.slot0 = 0;
     u.ctx = pos + 1;
     if (u.ctx <= 0) {
         for (int idx = threadIdx.x; idx < p.group * D; idx += kThreads)
@@ -594,7 +689,17 @@ static hipError_t launch_tile(const PrefillParams& p, hipStream_t stream) {
     const size_t grid = (size_t)p.num_seqs * ntile * p.n_kv;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(prefill_tile_kernel, dim3((unsigned)grid), dim3(kTileThreads), 0, stream, p, ntile);
+    hipLaunchKernelGGL(prefill_tile_kernel<false>, dim3((unsigned)grid), dim3(kTileThreads), 0, stream, p, ntile);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefix(const PrefillParams& p, hipStream_t stream) {
+    if (p.group <= 0 || 32 % p.group != 0 || p.kpmax <= 0 || !p.plan) return hipErrorInvalidValue;
+    const int ts = kTileWaves * (32 / p.group);
+    const size_t grid = (size_t)((p.num_seqs + ts - 1) / ts) * p.kpmax * p.n_kv;
+    if (grid == 0) return hipSuccess;
+    if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(prefill_tile_kernel<true>, dim3((unsigned)grid), dim3(kTileThreads), 0, stream, p, 0);
     return hipGetLastError();
 }
 

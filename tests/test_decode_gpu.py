@@ -140,6 +140,64 @@ def test_shared_prefix_quantized_bitexact(lib, bits):
     assert_close(dev_to_f64(outs[0]), ref, "bf16", f"clusters int{bits}")
 
 
+# Batches of at least 512 query rows per KV head (bf16 pools, d 128, G
+# dividing 32) take the prefix pass: per tile of 256 / G consecutive
+# sequences, the leading run of blocks that every member holds at the same
+# ids (ending before the shortest member's last token, cut to whole 4-block
+# stages, at least 16 blocks) is attended by one MFMA contraction over the
+# tile's rows, its stages split into ranges; the decode covers the rest and
+# merges. The tiles below hold: a run that ends one token before a member's
+# end (41 blocks, cut to 40); two clusters with no common run (the other
+# paths); a run cut short by one member (20 of 100 shared blocks); a last
+# tile of four sequences whose 18-block run is cut to 16.
+def _prefix_tiles(G):
+    ts = 256 // G
+    return [
+        (41, [657] + [658 + (i * 97) % 900 for i in range(ts - 1)]),
+        (30, [500 + (i * 53) % 700 for i in range(ts // 2)]),
+        (60, [1000 + (i * 71) % 500 for i in range(ts - ts // 2)]),
+        (100, [325] + [1601 + (i * 37) % 400 for i in range(ts - 1)]),
+        (18, [289 + (i * 11) % 300 for i in range(4)]),
+    ]
+
+
+@pytest.mark.parametrize("n_heads,n_kv,pb", [
+    (64, 8, 0), (64, 8, 2), (64, 8, 16), (32, 8, 0), (64, 4, 0), (64, 4, 64), (16, 8, 0),
+])
+def test_prefix_pass_tiles(lib, n_heads, n_kv, pb):
+    G = n_heads // n_kv
+    c = make_clustered_prefix_case(n_heads, n_kv, 128, "bf16", _prefix_tiles(G), 340 + n_heads + pb)
+    assert c.num_seqs * G >= 512
+    _parity(c, partition_blocks=pb)
+
+
+def test_prefix_pass_workspace_reuse(lib):
+    """A workspace alternating between prefix-pass calls and calls without
+    it gives the same bits each time and leaves its counters zero."""
+    from paged_kv_cache_429_amd import binding as B
+    CB = 1 << 20
+    a = make_clustered_prefix_case(64, 8, 128, "bf16", _prefix_tiles(8), 351)
+    b = make_config_case(2, num_seqs=8)
+    n = max(B.lib().paged_attn_decode_workspace_size(x.num_seqs, x.n_heads, x.n_kv, 128, x.max_context_len, 0)
+            for x in (a, b))
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+
+    def run(x):
+        kp, vp = upload_pools(x)
+        t, cl = upload_meta(x)
+        o = B.decode(np_to_dev(x.q, "bf16"), kp, vp, t, cl, n_kv_heads=x.n_kv, max_context_len=x.max_context_len,
+                     workspace=ws).clone()
+        torch.cuda.synchronize()
+        assert int(ws[:CB].count_nonzero()) == 0
+        return o
+
+    outs = [run(a), run(b), run(a), run(b)]
+    assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
+    assert torch.equal(outs[1].view(torch.int16), outs[3].view(torch.int16))
+    assert_close(dev_to_f64(outs[0]), oracle_decode(a), "bf16", "prefix pass")
+    assert_close(dev_to_f64(outs[1]), oracle_decode(b), "bf16", "after prefix pass")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("kind", ["nan", "big"])
 def test_poisoned_unused_slots(lib, dtype, kind):
