@@ -22,6 +22,11 @@ Prefill chunk ([JE] "Chunked prefill"; [TAI] "Scheduling prefill and decode"):
 the same attention split into pieces; query i of a chunk of q_len tokens sits
 at absolute position ctx - q_len + i and attends to keys 0..position
 (inclusive).
+
+Sliding window ([IR] "The memory equation" lists sliding-window attention
+among the ways to shrink the cache, with no formula): read as the query at
+position p attending only the last W tokens, keys p - W + 1 .. p, so W = 1
+is the token itself and W >= p + 1 is full attention.
 """
 from __future__ import annotations
 
@@ -59,12 +64,15 @@ def softmax_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float)
 
 
 def paged_decode(q, k_pool, v_pool, block_tables, context_lens, *, n_kv: int,
-                 block_size: int = BLOCK, scale: float | None = None, seqs=None) -> np.ndarray:
+                 block_size: int = BLOCK, scale: float | None = None, seqs=None,
+                 window: int | None = None) -> np.ndarray:
     """Decode attention for every sequence (or the listed `seqs`).
 
     q [S, H, D] float64; k_pool/v_pool [num_blocks*block_size, n_kv, D]
     float64; returns float64 [S, H, D] (rows of unlisted sequences are NaN).
-    A sequence with context length 0 gets a zero output row.
+    A sequence with context length 0 gets a zero output row. With a window W
+    the query (the last token, position n - 1) attends tokens max(0, n - W)
+    .. n - 1 only.
     """
     q = np.asarray(q, dtype=np.float64)
     S, H, D = q.shape
@@ -79,6 +87,9 @@ def paged_decode(q, k_pool, v_pool, block_tables, context_lens, *, n_kv: int,
             continue
         K = gather(k_pool, block_tables[s], n, block_size)  # [n, n_kv, D]
         V = gather(v_pool, block_tables[s], n, block_size)
+        if window is not None:
+            first = max(0, n - int(window))
+            K, V = K[first:], V[first:]
         for h in range(H):
             kvh = h // G
             out[s, h] = softmax_attention(q[s, h], K[:, kvh, :], V[:, kvh, :], scale)

@@ -24,17 +24,19 @@ def _f16(x: float) -> float:
         return math.copysign(math.inf, x)
 
 
-def decode_attention(q, k_pool, v_pool, table, n_ctx, n_kv, block_size=16):
+def decode_attention(q, k_pool, v_pool, table, n_ctx, n_kv, block_size=16, window=None):
     """q: nested lists [H][D]; pools: nested lists [slot][n_kv][D].
-    Returns [H][D] with scale 1/sqrt(D), kv head = h // (H / n_kv)."""
+    Returns [H][D] with scale 1/sqrt(D), kv head = h // (H / n_kv). With a
+    window W only the tokens t with n_ctx - W <= t < n_ctx are attended."""
     H = len(q)
     D = len(q[0])
     G = H // n_kv
+    first = 0 if window is None else max(0, n_ctx - window)
     out = []
     for h in range(H):
         kvh = h // G
         scores = []
-        for t in range(n_ctx):
+        for t in range(first, n_ctx):
             slot = table[t // block_size] * block_size + t % block_size
             dot = 0.0
             for i in range(D):
@@ -44,10 +46,10 @@ def decode_attention(q, k_pool, v_pool, table, n_ctx, n_kv, block_size=16):
         w = [math.exp(z - m) for z in scores]
         tot = sum(w)
         row = [0.0] * D
-        for t in range(n_ctx):
+        for t in range(first, n_ctx):
             slot = table[t // block_size] * block_size + t % block_size
             for i in range(D):
-                row[i] += w[t] / tot * v_pool[slot][kvh][i]
+                row[i] += w[t - first] / tot * v_pool[slot][kvh][i]
         out.append(row)
     return out
 

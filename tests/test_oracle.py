@@ -61,6 +61,61 @@ def test_oracle_vs_brute_force_random_tiny(seed):
         np.testing.assert_allclose(out[s], np.array(ref), rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_window_vs_brute_force_random_tiny(seed):
+    """Sliding window W: keys n - W .. n - 1 only (brute force, windows from 1
+    to past the context)."""
+    g = np.random.default_rng(50 + seed)
+    n_kv, G, d = int(g.choice([1, 2])), int(g.choice([1, 2, 4])), int(g.choice([4, 8]))
+    ctx = g.integers(1, 60, size=3)
+    c = make_decode_case(n_kv * G, n_kv, d, "bf16" if seed % 2 else "f32", ctx, 150 + seed, pool_factor=1.5)
+    q, k, v = f64(c, c.q), f64(c, c.k_slots), f64(c, c.v_slots)
+    for w in (1, 2, 15, 16, 17, 33, 70):
+        out = oracle.paged_decode(q, k, v, c.block_tables, c.context_lens, n_kv=n_kv, window=w)
+        for s in range(c.num_seqs):
+            ref = brute.decode_attention(q[s].tolist(), k.tolist(), v.tolist(), c.block_tables[s].tolist(),
+                                         int(c.context_lens[s]), n_kv, window=w)
+            np.testing.assert_allclose(out[s], np.array(ref), rtol=0, atol=1e-12)
+
+
+def test_window_one_is_last_value():
+    """A window of one token: the softmax has one term, so the output is
+    exactly that token's V."""
+    c = make_decode_case(8, 2, 32, "bf16", [1, 17, 40, 100], 9, pool_factor=1.2)
+    q, k, v = f64(c, c.q), f64(c, c.k_slots), f64(c, c.v_slots)
+    out = oracle.paged_decode(q, k, v, c.block_tables, c.context_lens, n_kv=2, window=1)
+    for s in range(c.num_seqs):
+        t = int(c.context_lens[s]) - 1
+        slot = c.block_tables[s, t // 16] * 16 + t % 16
+        for h in range(8):
+            assert np.array_equal(out[s, h], v[slot, h // 4])
+
+
+def test_window_equals_truncated_context():
+    """Decode with window W equals full decode of a sequence that holds only
+    its last W tokens (copied into fresh blocks, starting at slot 0), and a
+    window covering the context changes nothing."""
+    c = make_decode_case(8, 4, 16, "f32", [5, 31, 64, 77], 10, pool_factor=1.3)
+    q, k, v = f64(c, c.q), f64(c, c.k_slots), f64(c, c.v_slots)
+    full = run_decode(c)
+    for w in (3, 16, 20, 64, 200):
+        got = oracle.paged_decode(q, k, v, c.block_tables, c.context_lens, n_kv=4, window=w)
+        for s in range(c.num_seqs):
+            n = int(c.context_lens[s])
+            if w >= n:
+                assert np.array_equal(got[s], full[s])
+            m = min(w, n)
+            toks = np.arange(n - m, n)
+            slots = c.block_tables[s, toks // 16].astype(np.int64) * 16 + toks % 16
+            nb = -(-m // 16)
+            table = np.arange(nb, dtype=np.int32)[None, :]
+            kk = np.zeros((nb * 16,) + k.shape[1:])
+            vv = np.zeros_like(kk)
+            kk[:m], vv[:m] = k[slots], v[slots]
+            ref = oracle.paged_decode(q[s:s + 1], kk, vv, table, np.array([m]), n_kv=4)
+            np.testing.assert_allclose(got[s], ref[0], rtol=0, atol=1e-14)
+
+
 def test_closed_form_single_token():
     c = make_decode_case(8, 2, 32, "f32", [1, 1, 1], 7)
     out = run_decode(c)
