@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--workload", default="2")
     ap.add_argument("--layers", type=int, default=4, help="copies of the layer's pools cycled through")
     ap.add_argument("--partition-blocks", type=int, default=0)
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window in tokens for the decode workloads (0: full attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -114,13 +116,20 @@ def measured_traffic(profile):
     return int(vals["traffic_bytes_per_launch"])
 
 
-def decode_bytes(case, kv_bits):
+def decode_bytes(case, kv_bits, window=0):
     """Algorithmic bytes of one decode step: every attended token's K and V
-    once per KV head (shared blocks once), scales, Q, O, table entries, lengths."""
+    once per KV head (shared blocks once), scales, Q, O, table entries, lengths.
+    With a sliding window only the last `window` tokens of each sequence are
+    attended, and only the blocks holding them are looked up."""
     n_kv, d = case.n_kv, case.d
     ctx = case.context_lens.astype(np.int64)
     nblk = -(-ctx // 16)
-    if case.shared_prefix_blocks:
+    if window:
+        first_blk = np.maximum(ctx - window, 0) // 16
+        tokens = int(np.minimum(ctx, window).sum())
+        blocks = int((nblk - first_blk).sum())
+        nblk = nblk - first_blk
+    elif case.shared_prefix_blocks:
         P = case.shared_prefix_blocks
         tokens = P * 16 + int(np.sum(ctx - P * 16))
         blocks = P + int(np.sum(nblk - P))
@@ -152,7 +161,7 @@ def to_dev(x, dtype, torch):
     return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
 
 
-def cpu_baseline(case, kv_bits, budget_s):
+def cpu_baseline(case, kv_bits, budget_s, window=0):
     """The oracle, as it stands, on whole sequences of the same workload until
     about `budget_s` seconds of host time; throughput in the metric's unit.
     Decoding the pools to float64 (and quantizing them, for int KV) is
@@ -171,10 +180,13 @@ def cpu_baseline(case, kv_bits, budget_s):
     t0 = time.perf_counter()
     while time.perf_counter() - t0 <= budget_s:  # whole sequences, repeating the batch if it is short
         s = int(order[len(done) % len(order)])
-        oracle.paged_decode(q, kf, vf, case.block_tables, case.context_lens, n_kv=case.n_kv, seqs=[s])
+        oracle.paged_decode(q, kf, vf, case.block_tables, case.context_lens, n_kv=case.n_kv, seqs=[s],
+                            window=window or None)
         done.append(s)
     el = time.perf_counter() - t0
     sub = case.context_lens[done].astype(np.int64)
+    if window:
+        sub = np.minimum(sub, window)
     per_tok = case.n_kv * case.d * 2 * kv_bits / 8
     elem = 2 if case.dtype == "bf16" else 4
     byts = float(sub.sum()) * per_tok + 2 * len(done) * case.n_heads * case.d * elem
@@ -184,7 +196,7 @@ def cpu_baseline(case, kv_bits, budget_s):
         "cores": _CORES,
         "kind": "oracle",
         "sample": (f"{len(done)} sequence decodes drawn from the {case.num_seqs}-sequence batch "
-                   f"({int(sub.sum())} context tokens) in {el:.1f} s; float64 NumPy, all heads"),
+                   f"({int(sub.sum())} attended tokens) in {el:.1f} s; float64 NumPy, all heads"),
         "seqs_per_s": round(len(done) / el, 3),
     }
 
@@ -355,7 +367,8 @@ def main():
     def step(i):
         k_, v_, ks_, vs_ = layers[i % len(layers)]
         B.decode(q, k_, v_, tables, ctx, n_kv_heads=case.n_kv, max_context_len=mcl, kv_bits=kv_bits,
-                 k_scales=ks_, v_scales=vs_, out=out, workspace=ws, partition_blocks=a.partition_blocks)
+                 k_scales=ks_, v_scales=vs_, out=out, workspace=ws, partition_blocks=a.partition_blocks,
+                 window=a.window or None)
 
     for i in range(a.warmup):
         step(i)
@@ -372,13 +385,15 @@ def main():
     wall = time.perf_counter() - t0
     kern_ms = np.array([s.elapsed_time(e) for s, e in ev])
 
-    byts = decode_bytes(case, kv_bits)
+    byts = decode_bytes(case, kv_bits, a.window)
     ms_step = wall * 1e3 / a.steps
     value = byts / (ms_step * 1e-3) / 1e9
     k_avg = float(kern_ms.mean())
     achieved = byts / (k_avg * 1e-3) / 1e9
     name = {"2": 2, "3": 3, "4a": 4, "4b": 4, "5d": 5}[a.workload]
     wl = CONFIGS[name]["workload"] + ({"4a": " [int8]", "4b": " [int4]", "5d": " [decode half]"}.get(a.workload, ""))
+    if a.window:
+        wl += f" [sliding window {a.window}]"
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -396,7 +411,7 @@ def main():
             "workload": wl,
             "num_seqs": case.num_seqs, "n_heads": case.n_heads, "n_kv_heads": case.n_kv, "d_head": case.d,
             "block_size": 16, "kv_bits": kv_bits, "total_context_tokens": int(case.context_lens.sum()),
-            "max_context_len": mcl, "seed": case.seed, "layers_cycled": a.layers,
+            "max_context_len": mcl, "seed": case.seed, "layers_cycled": a.layers, "window": a.window,
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s_per_layer": round(case.num_seqs / (ms_step * 1e-3), 1),
@@ -411,7 +426,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(PROFILE_NAME[a.workload]),
+            "traffic": measured_traffic(PROFILE_NAME[a.workload] + (f"_window{a.window}" if a.window else "")),
             "kernel_avg_us": round(k_avg * 1e3, 3),
             "kernel_p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
             "kernel_p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 3),
@@ -419,7 +434,7 @@ def main():
         "input_generation_s": round(gen_s, 2),
     }
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(case, kv_bits, a.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(case, kv_bits, a.cpu_seconds, a.window)
     print(json.dumps(res), flush=True)
 
 

@@ -3,6 +3,7 @@
  *
  * A C ABI over hand-written HIP kernels:
  *   paged_attn_decode         single-query attention of a batch of sequences
+ *   paged_attn_decode_window  the same over each sequence's last W tokens
  *   paged_attn_prefill_chunk  causal attention of a chunk of prompt tokens
  *   kv_quantize               symmetric int8 / int4 codes + fp16 scales
  *   paged_kv_write            scatter new tokens' K/V into their cache slots
@@ -186,6 +187,27 @@ int paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
                       int n_heads, int n_kv_heads, int d_head, int dtype, int kv_bits,
                       void* out, void* workspace, size_t workspace_bytes,
                       int partition_blocks, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Sliding-window decode ([IR] "The memory equation": sliding-window attention
+ * is one of the ways to shrink the cache; the pages give no formula). The
+ * query of sequence s (its last token, position ctx_s - 1) attends only the
+ * last window_tokens tokens, positions max(0, ctx_s - window_tokens) ..
+ * ctx_s - 1; a window of at least ctx_s is full attention.
+ * Arguments as for paged_attn_decode (same workspace size), plus
+ * window_tokens >= 1 (else PA_ERR_INVALID_ARG). Only the blocks holding
+ * attended tokens are read (table entries before them are not). The
+ * shared-prefix mechanisms are not used: every sequence is computed on its
+ * own.
+ * ------------------------------------------------------------------------ */
+int paged_attn_decode_window(const void* q, const void* k_pool, const void* v_pool,
+                             const uint16_t* k_scales, const uint16_t* v_scales,
+                             const int32_t* block_tables, int max_blocks_per_seq,
+                             const int32_t* context_lens, int max_context_len,
+                             int num_seqs, int num_blocks, int block_size,
+                             int n_heads, int n_kv_heads, int d_head, int dtype, int kv_bits,
+                             void* out, void* workspace, size_t workspace_bytes,
+                             int partition_blocks, int window_tokens, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Causal prefill of a chunk ([JE] "Chunked prefill"; [TAI] "Scheduling

@@ -23,7 +23,7 @@ BLOCK_SIZE = 16
 # every function declared in include/paged_attn.h
 EXPORTS = (
     "pa_error_string", "pa_tile_bytes", "pa_kv_bytes_per_token", "pa_kv_cache_bytes",
-    "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_prefill_chunk",
+    "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_decode_window", "paged_attn_prefill_chunk",
     "kv_quantize", "paged_kv_write",
 )
 
@@ -49,6 +49,9 @@ def _declare(lib):
     lib.paged_attn_decode_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.paged_attn_decode.restype = i
     lib.paged_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, i, i, i, vp, vp, sz, i, vp]
+    lib.paged_attn_decode_window.restype = i
+    lib.paged_attn_decode_window.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, i, i, i, vp, vp, sz, i, i,
+                                             vp]
     lib.paged_attn_prefill_chunk.restype = i
     lib.paged_attn_prefill_chunk.argtypes = [vp, vp, i, i, vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, i, i, i,
                                              vp, vp]
@@ -165,8 +168,9 @@ def decode_workspace(num_seqs, n_heads, n_kv_heads, d_head, max_context_len, par
 
 
 def decode(q, k_pool, v_pool, block_tables, context_lens, *, n_kv_heads, max_context_len, kv_bits=None,
-           k_scales=None, v_scales=None, out=None, workspace=None, partition_blocks=0, stream=None):
-    """paged_attn_decode. q [S, H, D] (float32 or bfloat16); block_tables
+           k_scales=None, v_scales=None, out=None, workspace=None, partition_blocks=0, stream=None, window=None):
+    """paged_attn_decode, or paged_attn_decode_window when a window (tokens,
+    >= 1) is given. q [S, H, D] (float32 or bfloat16); block_tables
     [S, max_blocks] int32; context_lens [S] int32; returns out [S, H, D]."""
     dev = _gpu(q, k_pool, v_pool, block_tables, context_lens, k_scales, v_scales, out, workspace)
     S, H, D = q.shape
@@ -181,11 +185,14 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, *, n_kv_heads, max_con
     if workspace is None:
         workspace = decode_workspace(S, H, n_kv_heads, D, max_context_len, partition_blocks, dev, stream)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().paged_attn_decode(
-        _p(q), _p(k_pool), _p(v_pool), _p(k_scales), _p(v_scales), _p(block_tables), block_tables.shape[1],
-        _p(context_lens), int(max_context_len), S, nb, BLOCK_SIZE, H, n_kv_heads, D, dt, kv_bits,
-        _p(out), _p(workspace), wbytes, int(partition_blocks), _stream(stream, dev))
-    _check("paged_attn_decode", st)
+    args = (_p(q), _p(k_pool), _p(v_pool), _p(k_scales), _p(v_scales), _p(block_tables), block_tables.shape[1],
+            _p(context_lens), int(max_context_len), S, nb, BLOCK_SIZE, H, n_kv_heads, D, dt, kv_bits,
+            _p(out), _p(workspace), wbytes, int(partition_blocks))
+    if window is None:
+        _check("paged_attn_decode", lib().paged_attn_decode(*args, _stream(stream, dev)))
+    else:
+        _check("paged_attn_decode_window",
+               lib().paged_attn_decode_window(*args, int(window), _stream(stream, dev)))
     return out
 
 

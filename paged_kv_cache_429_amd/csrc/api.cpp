@@ -123,14 +123,17 @@ size_t paged_attn_decode_workspace_size(int num_seqs, int n_heads, int n_kv_head
     return pa::decode_workspace_bytes(num_seqs, n_heads, n_kv_heads, d_head, pmax, kpmax);
 }
 
-int paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
-                      const uint16_t* k_scales, const uint16_t* v_scales,
-                      const int32_t* block_tables, int max_blocks_per_seq,
-                      const int32_t* context_lens, int max_context_len,
-                      int num_seqs, int num_blocks, int block_size,
-                      int n_heads, int n_kv_heads, int d_head, int dtype, int kv_bits,
-                      void* out, void* workspace, size_t workspace_bytes,
-                      int partition_blocks, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both decode entry points; window 0 = none.
+int decode_impl(const void* q, const void* k_pool, const void* v_pool, const uint16_t* k_scales,
+                const uint16_t* v_scales, const int32_t* block_tables, int max_blocks_per_seq,
+                const int32_t* context_lens, int max_context_len, int num_seqs, int num_blocks, int block_size,
+                int n_heads, int n_kv_heads, int d_head, int dtype, int kv_bits, void* out, void* workspace,
+                size_t workspace_bytes, int partition_blocks, int window, void* stream) {
+    if (window < 0) return PA_ERR_INVALID_ARG;
     if (!valid_common(num_seqs, num_blocks, block_size, n_heads, n_kv_heads, d_head)) return PA_ERR_INVALID_ARG;
     if (max_blocks_per_seq <= 0 || max_context_len < 0) return PA_ERR_INVALID_ARG;
     if (partition_blocks < 0 || partition_blocks > 64 || (partition_blocks & 1)) return PA_ERR_INVALID_ARG;
@@ -166,13 +169,14 @@ int paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
     p.pb = plan_partition_blocks(num_seqs, n_kv_heads, std::max(1, max_context_len), partition_blocks);
     p.pmax = pa::num_parts(ceil_div(std::max(1, p.ctx_cap), PA_BLOCK_SIZE), p.pb);
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d_head));
+    p.window = window;
 
     // Shared-prefix workgroups (groups of 16/G consecutive sequences whose
     // tables name the same blocks fill the 16 MFMA columns) for the MFMA
     // formats at G = 4 or 8, when sequences can be split.
     p.share_n = 0;
     p.n_shared = 0;
-    if (fmt != 0 && p.pmax > 1) {
+    if (fmt != 0 && p.pmax > 1 && window == 0) {
         p.share_n = (G == 4 || G == 8) ? 16 / G : 0;
         if (p.share_n > 0) {
             const long n = (long)(num_seqs / p.share_n) * p.pmax * n_kv_heads;
@@ -183,7 +187,8 @@ int paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
     }
     // Prefix pass (bf16 pools): a launch before the decode that attends each
     // tile's common leading run of blocks for all its rows at once.
-    p.kpmax = fmt == 1 ? plan_prefix_parts(num_seqs, n_heads, n_kv_heads, d_head, p.ctx_cap, p.pmax) : 0;
+    p.kpmax = fmt == 1 && window == 0 ? plan_prefix_parts(num_seqs, n_heads, n_kv_heads, d_head, p.ctx_cap, p.pmax)
+                                      : 0;
     p.pslots = p.pmax + p.kpmax;
     p.prefix_ts = p.kpmax > 0 ? pa::kPrefixRows / G : 0;
     const size_t need = pa::decode_workspace_bytes(num_seqs, n_heads, n_kv_heads, d_head, p.pmax, p.kpmax);
@@ -221,6 +226,37 @@ int paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
     }
     const hipError_t e = pa::launch_decode(p, d_head, fmt, st);
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
+                      const uint16_t* k_scales, const uint16_t* v_scales,
+                      const int32_t* block_tables, int max_blocks_per_seq,
+                      const int32_t* context_lens, int max_context_len,
+                      int num_seqs, int num_blocks, int block_size,
+                      int n_heads, int n_kv_heads, int d_head, int dtype, int kv_bits,
+                      void* out, void* workspace, size_t workspace_bytes,
+                      int partition_blocks, void* stream) {
+    return decode_impl(q, k_pool, v_pool, k_scales, v_scales, block_tables, max_blocks_per_seq, context_lens,
+                       max_context_len, num_seqs, num_blocks, block_size, n_heads, n_kv_heads, d_head, dtype, kv_bits,
+                       out, workspace, workspace_bytes, partition_blocks, 0, stream);
+}
+
+int paged_attn_decode_window(const void* q, const void* k_pool, const void* v_pool,
+                             const uint16_t* k_scales, const uint16_t* v_scales,
+                             const int32_t* block_tables, int max_blocks_per_seq,
+                             const int32_t* context_lens, int max_context_len,
+                             int num_seqs, int num_blocks, int block_size,
+                             int n_heads, int n_kv_heads, int d_head, int dtype, int kv_bits,
+                             void* out, void* workspace, size_t workspace_bytes,
+                             int partition_blocks, int window_tokens, void* stream) {
+    if (window_tokens <= 0) return PA_ERR_INVALID_ARG;
+    return decode_impl(q, k_pool, v_pool, k_scales, v_scales, block_tables, max_blocks_per_seq, context_lens,
+                       max_context_len, num_seqs, num_blocks, block_size, n_heads, n_kv_heads, d_head, dtype, kv_bits,
+                       out, workspace, workspace_bytes, partition_blocks, window_tokens, stream);
 }
 
 int paged_attn_prefill_chunk(const void* q, const int32_t* cu_q_lens, int total_q, int max_q_len,

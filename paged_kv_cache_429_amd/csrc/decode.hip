@@ -94,14 +94,18 @@ void decode_kernel(DecodeParams p) {
         return;
     }
     u.nblk = (u.ctx + kBlock - 1) / kBlock;
-    // blocks [0, run) were attended by the prefix pass (run < nblk)
+    // blocks [0, run) were attended by the prefix pass (run < nblk); with a
+    // sliding window (never together with the prefix pass) the blocks
+    // before the one holding the window's first token are skipped
     const int run = p.prefix_ts > 0 ? p.plan[u.s / p.prefix_ts] : 0;
+    u.lo = p.window > 0 ? max(0, u.ctx - p.window) : 0;
+    const int b0 = p.window > 0 ? u.lo / kBlock : run;
     u.slot0 = prefix_parts(run, p.kpmax);
-    u.nparts = num_parts(u.nblk - run, p.pb);
+    u.nparts = num_parts(u.nblk - b0, p.pb);
     if (u.part >= u.nparts) return;
-    u.b_begin = run + u.part * p.pb;
-    u.b_end = run + part_end(u.nblk - run, p.pb, u.part, u.nparts);
-    if (p.share_n > 0 && run == 0) {  // taken by a shared-prefix workgroup?
+    u.b_begin = b0 + u.part * p.pb;
+    u.b_end = b0 + part_end(u.nblk - b0, p.pb, u.part, u.nparts);
+    if (p.share_n > 0 && b0 == 0) {  // taken by a shared-prefix workgroup?
         const int grp = u.s / p.share_n;
         if ((grp + 1) * p.share_n <= p.num_seqs && group_shares(p, grp * p.share_n, u.part)) return;
     }

@@ -29,9 +29,10 @@ struct WaveState {
 };
 
 // slot0: partial slots before this unit's partitions (the prefix pass's);
-// partition `part` stores its partial in slot slot0 + part.
+// partition `part` stores its partial in slot slot0 + part. lo: first
+// attended token (the sliding window's start, else 0).
 struct Unit {
-    int s, kvh, part, ctx, nblk, nparts, b_begin, b_end, slot0;
+    int s, kvh, part, ctx, nblk, nparts, b_begin, b_end, slot0, lo;
 };
 
 // Physical id of block j (wave-uniform, 0 <= j < 128) of a partition whose
@@ -278,15 +279,16 @@ __device__ __forceinline__ void pair_scores(const KHalf<D, FMT>& r, const u32x4*
 }
 
 // Scores in log2 units (c0, c1 fold 1/sqrt(d), log2 e and the K scales),
-// masked by select: tokens at or past ctx, and a missing second block, get
-// -inf. tok0 is the lane's first token (pair start + 4q).
+// masked by select: tokens at or past ctx or before lo (a sliding window's
+// start), and a missing second block, get -inf. tok0 is the lane's first
+// token (pair start + 4q).
 __device__ __forceinline__ void scale_mask(const f32x4& s0, const f32x4& s1, float c0, float c1, int tok0, int ctx,
-                                           bool has1, float* x) {
+                                           bool has1, int lo, float* x) {
     const int tok1 = tok0 + kBlock;
     // a pair wholly in context (the usual case; the test is wave-uniform,
     // as tok0 - 4q is) needs no select
     const int t0 = tok0 - 4 * ((threadIdx.x & 63) >> 4);
-    if (has1 && t0 + 2 * kBlock <= ctx) {
+    if (has1 && t0 >= lo && t0 + 2 * kBlock <= ctx) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             x[i] = s0[i] * c0;
@@ -296,8 +298,8 @@ __device__ __forceinline__ void scale_mask(const f32x4& s0, const f32x4& s1, flo
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        x[i] = (tok0 + i < ctx) ? s0[i] * c0 : kNegInf;
-        x[4 + i] = (has1 && tok1 + i < ctx) ? s1[i] * c1 : kNegInf;
+        x[i] = (tok0 + i < ctx && tok0 + i >= lo) ? s0[i] * c0 : kNegInf;
+        x[4 + i] = (has1 && tok1 + i < ctx && tok1 + i >= lo) ? s1[i] * c1 : kNegInf;
     }
 }
 
@@ -498,7 +500,7 @@ __device__ __forceinline__ void load_qop(const DecodeParams& p, int s, int qh, b
 // state unchanged. Returns the first pair after the run.
 template <int D, int FMT, bool NT, typename Ids, typename More, typename Geo>
 __device__ __forceinline__ int pair_run(const DecodeParams& p, int kvh, const u32x4* qop, ColState<D>& cs, int k,
-                                        Ids ids, More more, Geo geo, bool own = true) {
+                                        Ids ids, More more, Geo geo, bool own = true, int lo = 0) {
     const int q = (threadIdx.x & 63) >> 4;
     const float qoff = q_offset<D, FMT>(qop);
     KHalf<D, FMT> kr;
@@ -522,7 +524,7 @@ __device__ __forceinline__ int pair_run(const DecodeParams& p, int kvh, const u3
             s0 -= qoff;
             s1 -= qoff;
         }
-        scale_mask(s0, s1, c0, c1, t0 + 4 * q, ctx, has1, x);
+        scale_mask(s0, s1, c0, c1, t0 + 4 * q, ctx, has1, lo, x);
         if (!own) {  // a column of another sequence: no update
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = kNegInf;
@@ -564,7 +566,7 @@ constexpr int prefetch_pairs() {
 // state unchanged. Returns the first pair after the run.
 template <int D, int FMT, bool NT, int PD, typename Ids, typename Geo>
 __device__ __forceinline__ int pair_run_deep(const DecodeParams& p, int kvh, const u32x4* qop, ColState<D>& cs,
-                                             int k, int n, Ids ids, Geo geo, bool own = true) {
+                                             int k, int n, Ids ids, Geo geo, bool own = true, int lo = 0) {
     static_assert(PD == 1 || PD == 2, "prefetch distance");
     const int q = (threadIdx.x & 63) >> 4;
     const float qoff = q_offset<D, FMT>(qop);
@@ -601,7 +603,7 @@ __device__ __forceinline__ int pair_run_deep(const DecodeParams& p, int kvh, con
             s0 -= qoff;
             s1 -= qoff;
         }
-        scale_mask(s0, s1, c0, c1, t0 + 4 * q, ctx, has1, x);
+        scale_mask(s0, s1, c0, c1, t0 + 4 * q, ctx, has1, lo, x);
         if (!own) {  // a column of another sequence: no update
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = kNegInf;
@@ -672,9 +674,10 @@ __device__ __forceinline__ void mfma_wave(const DecodeParams& p, const Unit& u, 
             has1 = 2 * k + 1 < nb_part;
         };
         if constexpr (prefetch_pairs<FMT>() == 2) {
-            pair_run_deep<D, FMT, true, 2>(p, u.kvh, qop, cs, wave, (npairs - wave + kWaves - 1) / kWaves, ids, geo);
+            pair_run_deep<D, FMT, true, 2>(p, u.kvh, qop, cs, wave, (npairs - wave + kWaves - 1) / kWaves, ids, geo,
+                                           true, u.lo);
         } else {
-            pair_run<D, FMT, true>(p, u.kvh, qop, cs, wave, ids, [&](int k) { return k < npairs; }, geo);
+            pair_run<D, FMT, true>(p, u.kvh, qop, cs, wave, ids, [&](int k) { return k < npairs; }, geo, true, u.lo);
         }
     }
     col_to_lds<D, Mfma<D, FMT>::kOffset>(cs, st, wave);
@@ -746,7 +749,7 @@ __device__ __forceinline__ void f32_wave(const DecodeParams& p, const Unit& u, c
             }
         }
         const int tok = (u.b_begin + j) * kBlock + t;
-        const bool valid = tok < u.ctx;
+        const bool valid = tok < u.ctx && tok >= u.lo;
         float pt[16];
 #pragma unroll
         for (int g = 0; g < 16; ++g) {

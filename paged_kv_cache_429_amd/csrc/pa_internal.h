@@ -75,6 +75,7 @@ struct DecodeParams {
     int prefix_ts;      // sequences per prefix-pass tile (0: no prefix pass)
     int kpmax;          // prefix partitions per tile at most
     const int* plan;    // [tiles] run (blocks) the prefix pass covered, written by it
+    int window;         // sliding window in tokens (0: none): the last `window` tokens are attended
 };
 
 // Bytes of the arrival-counter region at the start of a decode workspace:

@@ -654,6 +654,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(PrefillParams pp)
     u.kvh = kvh;
     u.part = 0;
     u.slot0 = 0;
+    u.lo = 0;
     u.ctx = pos + 1;
     if (u.ctx <= 0) {
         for (int idx = threadIdx.x; idx < p.group * D; idx += kThreads)

@@ -41,22 +41,22 @@ def upload_meta(case):
             torch.from_numpy(np.ascontiguousarray(case.context_lens, dtype=np.int32)).cuda())
 
 
-def oracle_decode(case, seqs=None, k_slots=None, v_slots=None):
+def oracle_decode(case, seqs=None, k_slots=None, v_slots=None, window=None):
     k = oracle.as_f64(case.k_slots, case.dtype) if k_slots is None else k_slots
     v = oracle.as_f64(case.v_slots, case.dtype) if v_slots is None else v_slots
     return oracle.paged_decode(oracle.as_f64(case.q, case.dtype), k, v, case.block_tables, case.context_lens,
-                               n_kv=case.n_kv, seqs=seqs)
+                               n_kv=case.n_kv, seqs=seqs, window=window)
 
 
 def gpu_decode(case, kp=None, vp=None, partition_blocks=0, kv_bits=None, k_scales=None, v_scales=None,
-               max_context_len=None):
+               max_context_len=None, window=None):
     if kp is None:
         kp, vp = upload_pools(case)
     tables, ctx = upload_meta(case)
     q = np_to_dev(case.q, case.dtype)
     mcl = case.max_context_len if max_context_len is None else max_context_len
     out = B.decode(q, kp, vp, tables, ctx, n_kv_heads=case.n_kv, max_context_len=max(1, mcl), kv_bits=kv_bits,
-                   k_scales=k_scales, v_scales=v_scales, partition_blocks=partition_blocks)
+                   k_scales=k_scales, v_scales=v_scales, partition_blocks=partition_blocks, window=window)
     torch.cuda.synchronize()
     return out
 
