@@ -25,11 +25,16 @@ Pinning status (what each function is checked against lives in tests/):
                            invariance, causal probe.
   quantize.quantize_tiles  pinned: independent pure-Python brute force
                            (struct-based float32/float16 rounding), invariants.
+  quantize.*fp8, e4m3_*    pinned: the format's defining values, brute-force
+                           nearest search over all codes, ties, saturation,
+                           invariants of the quantized tiles.
   formulas.*               pinned: the pages' printed worked values.
   The softmax scale 1/sqrt(d_head) is a reading (the pages lose the formula);
   it is fixed by convention, not by a printed value.
 """
 from .attention import as_f64, paged_decode, paged_prefill, softmax_attention, gather  # noqa: F401
 from .quantize import quantize_tiles, dequantize, QMAX  # noqa: F401
+from .quantize import (E4M3_MAX, e4m3_value, e4m3_round, quantize_tiles_fp8,  # noqa: F401
+                       dequantize_fp8)
 from . import formulas  # noqa: F401
 from . import brute  # noqa: F401

@@ -83,3 +83,42 @@ def quantize_tile(values, bits):
         c = round(r)                  # Python round(): half to even
         codes.append(max(-qmax, min(qmax, c)))
     return codes, s
+
+
+def e4m3_table():
+    """(code, value) of the 127 non-negative finite OCP e4m3 codes, built with
+    math.ldexp from the bit fields: exponent field e (bias 7), mantissa m;
+    e == 0 gives the subnormal m / 8 * 2^-6."""
+    out = []
+    for code in range(0x7F):
+        e, m = code >> 3, code & 7
+        v = math.ldexp(m / 8.0, -6) if e == 0 else math.ldexp(1.0 + m / 8.0, e - 7)
+        out.append((code, v))
+    return out
+
+
+def quantize_tile_fp8(values):
+    """values: flat list of float32 numbers of one group. Returns (list of
+    e4m3 codes, fp16 scale as a Python float): s = fp16(fp32(amax / 448));
+    each code is the non-negative e4m3 value nearest |x / s| (searched over
+    every code, ties to the even code, beyond 448 saturating), with the sign
+    bit of x / s; all 0x00 when s is 0 or infinite."""
+    table = e4m3_table()
+    amax = 0.0
+    for x in values:
+        amax = max(amax, abs(x))
+    s = _f16(_f32(amax / 448.0))
+    codes = []
+    for x in values:
+        if s == 0.0 or math.isinf(s):
+            codes.append(0)
+            continue
+        r = _f32(x / s)
+        a = min(abs(r), 448.0)
+        best, best_d = None, None
+        for code, v in table:
+            d = abs(v - a)
+            if best is None or d < best_d or (d == best_d and code % 2 == 0):
+                best, best_d = code, d
+        codes.append(best | (0x80 if math.copysign(1.0, r) < 0 else 0))
+    return codes, s
