@@ -1,6 +1,6 @@
 """Benchmark: paged decode attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|3|4a|4b|5d|5p|5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|3|4a|4b|4f|5d|5p|5] [--no-cpu-baseline]
 
 A step is one paged_attn_decode call (all G query heads of every KV head,
 every sequence of the batch, split-context merge included) over one layer's
@@ -42,6 +42,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # counter summaries under profiles/ (name of the kernel and workload)
 PROFILE_NAME = {"2": "decode_kernel_llama3_8b_bf16", "3": "prefix_pass_and_decode_kernel_prefix_shared_70b_bf16",
                 "4a": "decode_kernel_quant_kv_70b_int8", "4b": "decode_kernel_quant_kv_70b_int4",
+                "4f": "decode_kernel_quant_kv_70b_fp8",
                 "5d": "decode_kernel_mixed_step_decode_bf16", "5p": "prefill_tile_kernel_chunk2048_ctx6000_bf16"}
 
 
@@ -116,6 +117,13 @@ def measured_traffic(profile):
     return int(vals["traffic_bytes_per_launch"])
 
 
+PA_KV_FP8 = 264  # kv_bits code of fp8 (e4m3) pools in the library's ABI
+
+
+def storage_bits(kv_bits):
+    return 8 if kv_bits == PA_KV_FP8 else kv_bits
+
+
 def decode_bytes(case, kv_bits, window=0):
     """Algorithmic bytes of one decode step: every attended token's K and V
     once per KV head (shared blocks once), scales, Q, O, table entries, lengths.
@@ -137,8 +145,8 @@ def decode_bytes(case, kv_bits, window=0):
         tokens = int(ctx.sum())
         blocks = int(nblk.sum())
     elem = 2 if case.dtype == "bf16" else 4
-    kv = tokens * n_kv * d * 2 * kv_bits / 8
-    scales = blocks * n_kv * 2 * 2 if kv_bits < 16 else 0
+    kv = tokens * n_kv * d * 2 * storage_bits(kv_bits) / 8
+    scales = blocks * n_kv * 2 * 2 if storage_bits(kv_bits) < 16 else 0
     qo = 2 * case.num_seqs * case.n_heads * d * elem
     meta = int(nblk.sum()) * 4 + case.num_seqs * 4
     return kv + scales + qo + meta
@@ -148,8 +156,8 @@ def build_case(workload):
     from synth import make_config_case, make_mixed_case
     if workload in ("2", "3"):
         return make_config_case(int(workload)), 16
-    if workload in ("4a", "4b"):
-        return make_config_case(4), 8 if workload == "4a" else 4
+    if workload in ("4a", "4b", "4f"):
+        return make_config_case(4), {"4a": 8, "4b": 4, "4f": PA_KV_FP8}[workload]
     if workload == "5d":
         return make_mixed_case()[1], 16
     raise SystemExit(f"unknown workload {workload}")
@@ -168,7 +176,12 @@ def cpu_baseline(case, kv_bits, budget_s, window=0):
     preparation and is not timed; gather + attention are."""
     import oracle
     q = oracle.as_f64(case.q, case.dtype)
-    if kv_bits < 16:
+    if kv_bits == PA_KV_FP8:
+        kc, ksc = oracle.quantize_tiles_fp8(oracle.as_f64(case.k_slots, case.dtype).astype(np.float32))
+        vc, vsc = oracle.quantize_tiles_fp8(oracle.as_f64(case.v_slots, case.dtype).astype(np.float32))
+        kf, vf = oracle.dequantize_fp8(kc, ksc), oracle.dequantize_fp8(vc, vsc)
+        del kc, vc
+    elif kv_bits < 16:
         kc, ksc = oracle.quantize_tiles(oracle.as_f64(case.k_slots, case.dtype).astype(np.float32), kv_bits)
         vc, vsc = oracle.quantize_tiles(oracle.as_f64(case.v_slots, case.dtype).astype(np.float32), kv_bits)
         kf, vf = oracle.dequantize(kc, ksc), oracle.dequantize(vc, vsc)
@@ -187,7 +200,7 @@ def cpu_baseline(case, kv_bits, budget_s, window=0):
     sub = case.context_lens[done].astype(np.int64)
     if window:
         sub = np.minimum(sub, window)
-    per_tok = case.n_kv * case.d * 2 * kv_bits / 8
+    per_tok = case.n_kv * case.d * 2 * storage_bits(kv_bits) / 8
     elem = 2 if case.dtype == "bf16" else 4
     byts = float(sub.sum()) * per_tok + 2 * len(done) * case.n_heads * case.d * elem
     return {
@@ -350,7 +363,7 @@ def main():
     B.kv_write(to_dev(case.k_slots, case.dtype, torch), to_dev(case.v_slots, case.dtype, torch), slots, kp, vp,
                n_kv_heads=case.n_kv)
     ks = vs = None
-    if kv_bits < 16:
+    if storage_bits(kv_bits) < 16:
         kp, ks = B.quantize(kp, bits=kv_bits, kind=0, n_kv_heads=case.n_kv, d_head=case.d)
         vp, vs = B.quantize(vp, bits=kv_bits, kind=1, n_kv_heads=case.n_kv, d_head=case.d)
     layers = [(kp, vp, ks, vs)]
@@ -390,8 +403,9 @@ def main():
     value = byts / (ms_step * 1e-3) / 1e9
     k_avg = float(kern_ms.mean())
     achieved = byts / (k_avg * 1e-3) / 1e9
-    name = {"2": 2, "3": 3, "4a": 4, "4b": 4, "5d": 5}[a.workload]
-    wl = CONFIGS[name]["workload"] + ({"4a": " [int8]", "4b": " [int4]", "5d": " [decode half]"}.get(a.workload, ""))
+    name = {"2": 2, "3": 3, "4a": 4, "4b": 4, "4f": 4, "5d": 5}[a.workload]
+    wl = CONFIGS[name]["workload"] + ({"4a": " [int8]", "4b": " [int4]", "4f": " [fp8 e4m3]",
+                                       "5d": " [decode half]"}.get(a.workload, ""))
     if a.window:
         wl += f" [sliding window {a.window}]"
     res = {
@@ -405,7 +419,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {32: "f32", 16: "bf16", 8: "bf16 q / int8 kv", 4: "bf16 q / int4 kv"}[kv_bits],
+        "dtype": {32: "f32", 16: "bf16", 8: "bf16 q / int8 kv", 4: "bf16 q / int4 kv",
+                  PA_KV_FP8: "bf16 q / fp8 e4m3 kv"}[kv_bits],
         "data": "synthetic",
         "config": {
             "workload": wl,

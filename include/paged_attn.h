@@ -62,17 +62,23 @@
  *   16  bfloat16           (requires dtype == PA_BF16)
  *    8  int8 code  + fp16 scale per (block, KV head) (requires PA_BF16)
  *    4  int4 code  + fp16 scale per (block, KV head) (requires PA_BF16)
+ *   PA_KV_FP8  OCP fp8 e4m3 code + fp16 scale per (block, KV head)
+ *              (requires PA_BF16; decode only). One byte per element, laid
+ *              out as int8; bit 7 sign, bits 6..3 exponent (bias 7), bits
+ *              2..0 mantissa, exponent 0 subnormal, 0x7F / 0xFF NaN.
  * A pool is an array of tiles, one per (block b, KV head h), each holding the
  * 16 slots x d_head elements of that block and head, at byte offset
- *     ((size_t)b * n_kv_heads + h) * tile_bytes,  tile_bytes = 16*d_head*kv_bits/8.
+ *     ((size_t)b * n_kv_heads + h) * tile_bytes,  tile_bytes = 16*d_head*bits/8,
+ * where bits is kv_bits, or 8 for PA_KV_FP8.
  * Inside a tile, element (slot t, dim i) is element number
- *     K pool:  ((i / x) * 16 + t) * x + i % x,   x = 128 / kv_bits
+ *     K pool:  ((i / x) * 16 + t) * x + i % x,   x = 128 / bits
  *              (16-byte chunks of x consecutive dims, slot-minor)
  *     V pool:  i * 16 + t                          (transposed: dim-major)
  * of the tile, elements packed at kv_bits each, little-endian; for int4 the
- * even-numbered element of a pair is the low nibble. Codes are two's
+ * even-numbered element of a pair is the low nibble. Integer codes are two's
  * complement. Scales are float16 bit patterns, k_scales / v_scales
- * [num_blocks][n_kv_heads]; value = code * scale.
+ * [num_blocks][n_kv_heads]; value = code * scale (for fp8, the code's e4m3
+ * value times the scale).
  * Supported d_head: 64 and 128.
  */
 #ifndef PAGED_ATTN_H
@@ -98,6 +104,8 @@ typedef enum pa_kv_kind { PA_KIND_K = 0, PA_KIND_V = 1 } pa_kv_kind;
 
 #define PA_BLOCK_SIZE 16
 #define PA_MAX_GROUP 16
+/* kv_bits code of OCP fp8 e4m3 pools (8 bits of storage per element). */
+#define PA_KV_FP8 264
 #define PA_DECODE_COUNTER_BYTES (1u << 20)
 
 /* Human-readable text of a status code (static storage). */
@@ -124,7 +132,8 @@ uint64_t pa_kv_cache_bytes(int n_layers, int n_kv_heads, int d_head, int kv_bits
  *
  * q            [num_seqs][n_heads][d_head] of dtype
  * k_pool/v_pool  pools in the layout above (read only)
- * k_scales/v_scales  fp16 [num_blocks][n_kv_heads]; NULL unless kv_bits < 16
+ * k_scales/v_scales  fp16 [num_blocks][n_kv_heads]; NULL unless kv_bits is
+ *              8, 4 or PA_KV_FP8
  * block_tables int32 [num_seqs][max_blocks_per_seq]
  * context_lens int32 [num_seqs]: tokens to attend, including the token being
  *              decoded (its K/V must already be in the pool). Values are
@@ -223,7 +232,8 @@ int paged_attn_decode_window(const void* q, const void* k_pool, const void* v_po
  * cu_q_lens     int32 [num_seqs + 1] device prefix sums, cu_q_lens[0] = 0,
  *               cu_q_lens[num_seqs] = total_q, 0 <= q_len_s <= max_q_len,
  *               q_len_s <= context_lens[s]
- * other arguments as for paged_attn_decode. No workspace.
+ * other arguments as for paged_attn_decode, except that fp8 pools
+ * (PA_KV_FP8) give PA_ERR_UNSUPPORTED. No workspace.
  * ------------------------------------------------------------------------ */
 int paged_attn_prefill_chunk(const void* q, const int32_t* cu_q_lens, int total_q, int max_q_len,
                              const void* k_pool, const void* v_pool,
@@ -242,8 +252,14 @@ int paged_attn_prefill_chunk(const void* q, const int32_t* cu_q_lens, int total_
  *   code = clamp( rint_half_even( x / float32(s) ), -qmax, qmax ), 0 if s == 0
  * (float32 IEEE division). src must be finite; a scale that overflows fp16
  * is stored as +inf with all codes 0.
+ * bits = PA_KV_FP8 (fp8, the format the pages name as the usual cache
+ * quantization: [TAI] "The KV cache"; [IR] "The debate"): qmax = 448, the
+ * largest finite e4m3 value, and the code is the e4m3 value nearest
+ * x / float32(s), ties to the even code, magnitudes past 448 saturating to
+ * 448, the sign of x kept (-0 is 0x80); all codes 0x00 when s is 0 or +inf.
+ * NaN codes are never written.
  * src     bf16 pool of `kind` (K or V layout, kv_bits = 16)
- * codes   int pool of the same kind with kv_bits = bits (written)
+ * codes   pool of the same kind with kv_bits = bits (written)
  * scales  fp16 [num_blocks][n_kv_heads] (written for the processed blocks)
  * block_ids  int32 [n_ids] blocks to process, or NULL for all num_blocks
  *            (ids outside [0, num_blocks) are skipped)

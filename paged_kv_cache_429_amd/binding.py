@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedatt
 PA_OK = 0
 PA_F32, PA_BF16 = 0, 1
 PA_KIND_K, PA_KIND_V = 0, 1
+PA_KV_FP8 = 264  # kv_bits code of OCP fp8 e4m3 pools
 BLOCK_SIZE = 16
 
 # every function declared in include/paged_attn.h

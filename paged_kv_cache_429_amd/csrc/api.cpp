@@ -27,11 +27,21 @@ int cu_count() {
     return n;
 }
 
+// kv_bits codes the library knows: 32, 16, 8, 4 and PA_KV_FP8.
+bool valid_kv_bits(int kv_bits) {
+    return kv_bits == 32 || kv_bits == 16 || kv_bits == 8 || kv_bits == 4 || kv_bits == PA_KV_FP8;
+}
+// Bits of storage per element of a kv_bits code.
+int storage_bits(int kv_bits) { return kv_bits == PA_KV_FP8 ? 8 : kv_bits; }
+// Quantized formats carry one fp16 scale per (block, KV head).
+bool quantized(int kv_bits) { return kv_bits == 8 || kv_bits == 4 || kv_bits == PA_KV_FP8; }
+
 int fmt_of(int dtype, int kv_bits) {
     if (dtype == PA_F32 && kv_bits == 32) return 0;
     if (dtype == PA_BF16 && kv_bits == 16) return 1;
     if (dtype == PA_BF16 && kv_bits == 8) return 2;
     if (dtype == PA_BF16 && kv_bits == 4) return 3;
+    if (dtype == PA_BF16 && kv_bits == PA_KV_FP8) return 4;
     return -1;
 }
 
@@ -95,20 +105,20 @@ const char* pa_error_string(int status) {
 }
 
 size_t pa_tile_bytes(int d_head, int kv_bits) {
-    if (d_head <= 0 || (kv_bits != 32 && kv_bits != 16 && kv_bits != 8 && kv_bits != 4)) return 0;
-    return (size_t)PA_BLOCK_SIZE * d_head * kv_bits / 8;
+    if (d_head <= 0 || !valid_kv_bits(kv_bits)) return 0;
+    return (size_t)PA_BLOCK_SIZE * d_head * storage_bits(kv_bits) / 8;
 }
 
 uint64_t pa_kv_bytes_per_token(int n_layers, int n_kv_heads, int d_head, int kv_bits) {
     if (n_layers <= 0 || n_kv_heads <= 0 || d_head <= 0 || kv_bits <= 0) return 0;
-    return 2ull * n_layers * n_kv_heads * (uint64_t)d_head * kv_bits / 8;
+    return 2ull * n_layers * n_kv_heads * (uint64_t)d_head * storage_bits(kv_bits) / 8;
 }
 
 uint64_t pa_kv_cache_bytes(int n_layers, int n_kv_heads, int d_head, int kv_bits, int64_t n_tokens) {
     if (n_layers <= 0 || n_kv_heads <= 0 || d_head <= 0 || n_tokens < 0) return 0;
-    if (kv_bits != 32 && kv_bits != 16 && kv_bits != 8 && kv_bits != 4) return 0;
+    if (!valid_kv_bits(kv_bits)) return 0;
     const uint64_t blocks = (uint64_t)((n_tokens + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE);
-    const uint64_t tile = (uint64_t)PA_BLOCK_SIZE * d_head * kv_bits / 8 + (kv_bits < 16 ? 2 : 0);
+    const uint64_t tile = (uint64_t)PA_BLOCK_SIZE * d_head * storage_bits(kv_bits) / 8 + (quantized(kv_bits) ? 2 : 0);
     return 2ull * n_layers * blocks * n_kv_heads * tile;
 }
 
@@ -139,14 +149,14 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool, const uin
     if (partition_blocks < 0 || partition_blocks > 64 || (partition_blocks & 1)) return PA_ERR_INVALID_ARG;
     const int fmt = fmt_of(dtype, kv_bits);
     if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID_ARG;
-    if (kv_bits != 32 && kv_bits != 16 && kv_bits != 8 && kv_bits != 4) return PA_ERR_INVALID_ARG;
+    if (!valid_kv_bits(kv_bits)) return PA_ERR_INVALID_ARG;
     if (fmt < 0) return PA_ERR_UNSUPPORTED;
     if (d_head != 64 && d_head != 128) return PA_ERR_UNSUPPORTED;
     const int G = n_heads / n_kv_heads;
     if (G > PA_MAX_GROUP) return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PA_OK;
     if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return PA_ERR_INVALID_ARG;
-    if (kv_bits < 16 && (!k_scales || !v_scales)) return PA_ERR_INVALID_ARG;
+    if (quantized(kv_bits) && (!k_scales || !v_scales)) return PA_ERR_INVALID_ARG;
     if (max_context_len == 0) max_context_len = 1;  // every row is then 0 or 1 token
 
     pa::DecodeParams p{};
@@ -270,15 +280,15 @@ int paged_attn_prefill_chunk(const void* q, const int32_t* cu_q_lens, int total_
     if (!valid_common(num_seqs, num_blocks, block_size, n_heads, n_kv_heads, d_head)) return PA_ERR_INVALID_ARG;
     if (max_blocks_per_seq <= 0 || max_context_len < 0 || total_q < 0 || max_q_len < 0) return PA_ERR_INVALID_ARG;
     if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID_ARG;
-    if (kv_bits != 32 && kv_bits != 16 && kv_bits != 8 && kv_bits != 4) return PA_ERR_INVALID_ARG;
+    if (!valid_kv_bits(kv_bits)) return PA_ERR_INVALID_ARG;
     const int fmt = fmt_of(dtype, kv_bits);
-    if (fmt < 0) return PA_ERR_UNSUPPORTED;
+    if (fmt < 0 || kv_bits == PA_KV_FP8) return PA_ERR_UNSUPPORTED;
     if (d_head != 64 && d_head != 128) return PA_ERR_UNSUPPORTED;
     const int G = n_heads / n_kv_heads;
     if (G > PA_MAX_GROUP) return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
     if (!q || !cu_q_lens || !k_pool || !v_pool || !block_tables || !context_lens || !out) return PA_ERR_INVALID_ARG;
-    if (kv_bits < 16 && (!k_scales || !v_scales)) return PA_ERR_INVALID_ARG;
+    if (quantized(kv_bits) && (!k_scales || !v_scales)) return PA_ERR_INVALID_ARG;
 
     pa::PrefillParams p{};
     p.q = q;
@@ -307,15 +317,16 @@ int paged_attn_prefill_chunk(const void* q, const int32_t* cu_q_lens, int total_
 int kv_quantize(const void* src, void* codes, uint16_t* scales, const int32_t* block_ids, int n_ids,
                 int num_blocks, int n_kv_heads, int block_size, int d_head, int bits, int kind, void* stream) {
     if (num_blocks <= 0 || n_kv_heads <= 0 || block_size != PA_BLOCK_SIZE || d_head <= 0) return PA_ERR_INVALID_ARG;
-    if (bits != 8 && bits != 4) return PA_ERR_INVALID_ARG;
+    if (bits != 8 && bits != 4 && bits != PA_KV_FP8) return PA_ERR_INVALID_ARG;
     if (kind != PA_KIND_K && kind != PA_KIND_V) return PA_ERR_INVALID_ARG;
     if (d_head != 64 && d_head != 128) return PA_ERR_UNSUPPORTED;
     if (block_ids && n_ids < 0) return PA_ERR_INVALID_ARG;
     const int n = block_ids ? n_ids : num_blocks;
     if (n == 0) return PA_OK;
     if (!src || !codes || !scales) return PA_ERR_INVALID_ARG;
-    const hipError_t e = pa::launch_quantize(src, codes, scales, block_ids, n, num_blocks, n_kv_heads, d_head, bits,
-                                             kind, static_cast<hipStream_t>(stream));
+    // the kernels take 0 for fp8 codes
+    const hipError_t e = pa::launch_quantize(src, codes, scales, block_ids, n, num_blocks, n_kv_heads, d_head,
+                                             bits == PA_KV_FP8 ? 0 : bits, kind, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

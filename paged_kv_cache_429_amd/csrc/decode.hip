@@ -21,7 +21,7 @@
 // log-sum-exp reduction in partition order and re-arms its arrival counter,
 // so one launch does the whole step.
 //
-// MFMA formulation (bf16 / int8 / int4 KV). Per pair of blocks:
+// MFMA formulation (bf16 / int8 / int4 / fp8 KV). Per pair of blocks:
 //   S^T[32 tok x 16 col] = K[tok x d] * Q^T[d x col]   (2 x D/32 MFMA 16x16x32)
 //   O^T[d x col]        += V^T[d x 32 tok] * P^T[32 tok x col] (D/16 MFMA)
 // The 16 columns are the G query heads of the KV head (zero-padded). The K
@@ -40,7 +40,7 @@ namespace pa {
 
 // Waves per SIMD the register budget is sized for: the bf16 loop fits three
 // (<= 168 VGPRs); the int4 loop, with two pairs in flight, needs more (int8
-// stays under 168 and runs at three anyway).
+// and fp8 stay under 168 and run at three anyway).
 template <int FMT>
 constexpr int decode_waves_per_eu() {
     return FMT == FMT_BF16 ? 3 : 2;
@@ -172,6 +172,7 @@ hipError_t launch_decode(const DecodeParams& p, int d, int fmt, hipStream_t stre
             case FMT_BF16: return launch_t<128, FMT_BF16>(p, stream);
             case FMT_I8: return launch_t<128, FMT_I8>(p, stream);
             case FMT_I4: return launch_t<128, FMT_I4>(p, stream);
+            case FMT_F8: return launch_t<128, FMT_F8>(p, stream);
         }
     } else if (d == 64) {
         switch (fmt) {
@@ -179,6 +180,7 @@ hipError_t launch_decode(const DecodeParams& p, int d, int fmt, hipStream_t stre
             case FMT_BF16: return launch_t<64, FMT_BF16>(p, stream);
             case FMT_I8: return launch_t<64, FMT_I8>(p, stream);
             case FMT_I4: return launch_t<64, FMT_I4>(p, stream);
+            case FMT_F8: return launch_t<64, FMT_F8>(p, stream);
         }
     }
     return hipErrorInvalidValue;

@@ -1,11 +1,15 @@
-// Cache-side kernels for gfx950: symmetric int8/int4 quantization of a bf16
-// pool, and scattering new tokens' K/V into their slots.
+// Cache-side kernels for gfx950: symmetric int8/int4/fp8 quantization of a
+// bf16 pool, and scattering new tokens' K/V into their slots.
 //
 // Quantization ("jovanaeducation" inference guide a2-inf-2, section
 // "KV-cache quantization": every key/value is an integer sharing one scale
 // with its group). Group = one (block, KV head) tile of 16 slots x d dims:
 //   s = fp16_rne(amax / qmax), code = clamp(rint(x / float(s)), -qmax, qmax)
 // with IEEE float32 division and round-half-to-even (v_rndne_f32).
+// fp8 (OCP e4m3; the pages name fp8 as the usual choice for the cache, "KV
+// cache, continuous batching and paged attention", section "The KV cache"):
+//   s = fp16_rne(amax / 448), code = e4m3 nearest x / float(s), ties to the
+//   even code, saturating at +-448, sign of x kept; all 0 if s is 0 or inf.
 //
 // Slot writes ("KV cache, continuous batching and paged attention", section
 // "The KV cache": each step computes K/V only for the new token and caches
@@ -19,6 +23,28 @@ namespace pa {
 // element number of (slot t, dim i) inside a K tile, x elements per 16 bytes
 __device__ __forceinline__ int k_elem(int t, int i, int x) { return ((i / x) * 16 + t) * x + i % x; }
 
+// e4m3 code of float32 r (finite): magnitudes from 448 up saturate to 448
+// (0x7E); below the smallest normal 2^-6 the code is the multiple of 2^-9
+// nearest |r| (rint of |r| * 512, exact, 0..8, where 8 is 2^-6's code);
+// otherwise r's exponent and mantissa are rounded to 3 mantissa bits, ties
+// to even, in integer arithmetic on the float's bits (a carry moves into the
+// exponent), and the exponent rebiased from 127 to 7.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float r) {
+    const uint32_t sign = (__float_as_uint(r) >> 24) & 0x80u;
+    const float a = fabsf(r);
+    uint32_t mag;
+    if (a >= 448.f) {
+        mag = 0x7Eu;
+    } else if (a < 0.015625f) {
+        mag = (uint32_t)__builtin_rintf(a * 512.f);
+    } else {
+        const uint32_t b = __float_as_uint(a);
+        mag = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);
+    }
+    return sign | mag;
+}
+
+// BITS 8 or 4 (integer codes) or 0 (fp8 e4m3 codes, one byte each).
 template <int D, int BITS, int KIND>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ src, uint8_t* __restrict__ codes,
                                                       uint16_t* __restrict__ scales, const int32_t* __restrict__ ids,
@@ -38,18 +64,21 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
 
-    constexpr float qmax = (BITS == 8) ? 127.f : 7.f;
+    constexpr bool F8 = (BITS == 0);
+    constexpr int CB = F8 ? 8 : BITS;              // bits per code
+    constexpr float qmax = F8 ? 448.f : (BITS == 8) ? 127.f : 7.f;
     const float s32 = amax / qmax;                 // IEEE division
     const _Float16 s16 = (_Float16)s32;            // round to nearest even
     const float sf = (float)s16;
     if (lane == 0) scales[(size_t)b * n_kv + h] = __builtin_bit_cast(uint16_t, s16);
-    const bool zero = !(sf > 0.f);                 // s == 0: all codes 0
+    // s == 0 (and, for fp8, s == inf): all codes 0
+    const bool zero = !(sf > 0.f) || (F8 && __builtin_isinf(sf));
 
     auto code_of = [&](int n) -> int {
         // element n of the int tile -> (slot, dim) -> source element
         int tt, ii;
         if (KIND == 0) {
-            constexpr int x = 128 / BITS;
+            constexpr int x = 128 / CB;
             const int c = n / (16 * x);
             tt = (n / x) % 16;
             ii = c * x + n % x;
@@ -60,15 +89,19 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
         const int se = (KIND == 0) ? k_elem(tt, ii, 8) : ii * 16 + tt;
         if (zero) return 0;
         const float r = bf16_bits_to_f32(t[se]) / sf;
-        float c = __builtin_rintf(r);
-        c = fminf(fmaxf(c, -qmax), qmax);
-        return (int)c;
+        if constexpr (F8) {
+            return (int)f32_to_e4m3(r);
+        } else {
+            float c = __builtin_rintf(r);
+            c = fminf(fmaxf(c, -qmax), qmax);
+            return (int)c;
+        }
     };
 
-    uint8_t* out = codes + ((size_t)b * n_kv + h) * (N * BITS / 8);
-    for (int o = lane; o < N * BITS / 8; o += 64) {
-        if (BITS == 8) {
-            out[o] = (uint8_t)(int8_t)code_of(o);
+    uint8_t* out = codes + ((size_t)b * n_kv + h) * (N * CB / 8);
+    for (int o = lane; o < N * CB / 8; o += 64) {
+        if (CB == 8) {
+            out[o] = (uint8_t)code_of(o);
         } else {
             const int lo = code_of(2 * o) & 0xf;
             const int hi = code_of(2 * o + 1) & 0xf;
@@ -95,8 +128,8 @@ hipError_t launch_quantize(const void* src, void* codes, uint16_t* scales, const
 #define PA_Q(DD, BB, KK) \
     if (d == DD && bits == BB && kind == KK) \
         return quant_t<DD, BB, KK>(src, codes, scales, block_ids, n_ids, num_blocks, n_kv, stream);
-    PA_Q(128, 8, 0) PA_Q(128, 8, 1) PA_Q(128, 4, 0) PA_Q(128, 4, 1)
-    PA_Q(64, 8, 0) PA_Q(64, 8, 1) PA_Q(64, 4, 0) PA_Q(64, 4, 1)
+    PA_Q(128, 8, 0) PA_Q(128, 8, 1) PA_Q(128, 4, 0) PA_Q(128, 4, 1) PA_Q(128, 0, 0) PA_Q(128, 0, 1)
+    PA_Q(64, 8, 0) PA_Q(64, 8, 1) PA_Q(64, 4, 0) PA_Q(64, 4, 1) PA_Q(64, 0, 0) PA_Q(64, 0, 1)
 #undef PA_Q
     return hipErrorInvalidValue;
 }

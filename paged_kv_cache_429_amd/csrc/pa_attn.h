@@ -58,7 +58,7 @@ struct Mfma {
     // First dim of the 8 consecutive dims lane group q feeds at k-step kk.
     __device__ static __forceinline__ int dbase(int kk, int q) {
         if (FMT == FMT_BF16) return 32 * kk + 8 * q;
-        if (FMT == FMT_I8) return 64 * (kk >> 1) + 16 * q + 8 * (kk & 1);
+        if (FMT == FMT_I8 || FMT == FMT_F8) return 64 * (kk >> 1) + 16 * q + 8 * (kk & 1);
         return (D == 128 ? 32 : 16) * q + 8 * kk;  // int4
     }
 
@@ -131,6 +131,13 @@ struct Mfma {
             a[1] = lo[1];
             a[2] = hi[0];
             a[3] = hi[1];
+        } else if (FMT == FMT_F8) {
+            const u32x2 lo = f8x4_to_bf16x4(r.w[2 * kk]);
+            const u32x2 hi = f8x4_to_bf16x4(r.w[2 * kk + 1]);
+            a[0] = lo[0];
+            a[1] = lo[1];
+            a[2] = hi[0];
+            a[3] = hi[1];
         } else {
             a = i4x8_to_bf16x8(r.w[kk]);
         }
@@ -147,7 +154,7 @@ struct Mfma {
                 u32x2 v = ld<NT>(reinterpret_cast<const u32x2*>(tile + d * 32 + q * 8));
                 r.w[2 * nb] = v[0];
                 r.w[2 * nb + 1] = v[1];
-            } else if (FMT == FMT_I8) {
+            } else if (FMT == FMT_I8 || FMT == FMT_F8) {
                 r.w[nb] = ld<NT>(reinterpret_cast<const uint32_t*>(tile + d * 16 + q * 4));
             } else {
                 r.w[nb] = ld<NT>(reinterpret_cast<const uint16_t*>(tile + d * 8 + q * 2));
@@ -159,7 +166,7 @@ struct Mfma {
     // for dim row nb*16 + l16, the 8 consecutive tokens 8 (q % 2) .. + 7 of
     // the pair's block q / 2 -- one contiguous run of a V tile row (16, 8 or
     // 4 bytes), so each load instruction moves 1 KiB, 512 B or 256 B.
-    static constexpr int VPDW = (FMT == FMT_BF16) ? 4 : (FMT == FMT_I8 ? 2 : 1);  // dwords per nb
+    static constexpr int VPDW = (FMT == FMT_BF16) ? 4 : (FMT == FMT_I8 || FMT == FMT_F8 ? 2 : 1);  // dwords per nb
     struct VPairRaw { uint32_t w[NB * VPDW]; };
 
     template <bool NT = true>
@@ -177,7 +184,7 @@ struct Mfma {
                 r.w[4 * nb + 1] = v[1];
                 r.w[4 * nb + 2] = v[2];
                 r.w[4 * nb + 3] = v[3];
-            } else if (FMT == FMT_I8) {
+            } else if (FMT == FMT_I8 || FMT == FMT_F8) {
                 const u32x2 v = ld<NT>(reinterpret_cast<const u32x2*>(a));
                 r.w[2 * nb] = v[0];
                 r.w[2 * nb + 1] = v[1];
@@ -195,6 +202,13 @@ struct Mfma {
             a[1] = r.w[4 * nb + 1];
             a[2] = r.w[4 * nb + 2];
             a[3] = r.w[4 * nb + 3];
+        } else if (FMT == FMT_F8) {
+            const u32x2 lo = f8x4_to_bf16x4(r.w[2 * nb]);
+            const u32x2 hi = f8x4_to_bf16x4(r.w[2 * nb + 1]);
+            a[0] = lo[0];
+            a[1] = lo[1];
+            a[2] = hi[0];
+            a[3] = hi[1];
         } else if (FMT == FMT_I8) {  // offset by kOff (see k_operand_dec)
             const u32x2 lo = i8x4_to_bf16x4_off128(r.w[2 * nb]);
             const u32x2 hi = i8x4_to_bf16x4_off128(r.w[2 * nb + 1]);
@@ -217,6 +231,8 @@ struct Mfma {
             return x;
         } else if (FMT == FMT_I8) {
             return i8x4_to_bf16x4(r.w[nb]);
+        } else if (FMT == FMT_F8) {
+            return f8x4_to_bf16x4(r.w[nb]);
         } else {
             return i4x4_to_bf16x4(r.w[nb]);
         }
@@ -431,7 +447,7 @@ __device__ __forceinline__ void issue_k_pair(const DecodeParams& p, int kvh, int
     M::template load_k<NT>(kbase + ((size_t)i0 * p.n_kv + kvh) * M::TILE, lane, r.k0);
     M::template load_k<NT>(kbase + ((size_t)i1 * p.n_kv + kvh) * M::TILE, lane, r.k1);
     r.s0 = r.s1 = 1.f;
-    if (FMT == FMT_I8 || FMT == FMT_I4) {
+    if (is_quant<FMT>()) {
         r.s0 = fp16_bits_to_f32(p.k_scales[(size_t)i0 * p.n_kv + kvh]);
         r.s1 = fp16_bits_to_f32(p.k_scales[(size_t)i1 * p.n_kv + kvh]);
     }
@@ -445,7 +461,7 @@ __device__ __forceinline__ void issue_v_pair(const DecodeParams& p, int kvh, int
     M::template load_v_pair<NT>(vbase + ((size_t)i0 * p.n_kv + kvh) * M::TILE,
                                 vbase + ((size_t)i1 * p.n_kv + kvh) * M::TILE, lane, r.v);
     r.s0 = r.s1 = 1.f;
-    if (FMT == FMT_I8 || FMT == FMT_I4) {
+    if (is_quant<FMT>()) {
         r.s0 = fp16_bits_to_f32(p.v_scales[(size_t)i0 * p.n_kv + kvh]);
         r.s1 = fp16_bits_to_f32(p.v_scales[(size_t)i1 * p.n_kv + kvh]);
     }

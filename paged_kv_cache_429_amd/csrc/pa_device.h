@@ -16,13 +16,17 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBlock = 16;   // tokens per physical block
 constexpr int kWave = 64;    // CDNA wavefront
 
-enum KvFmt { FMT_F32 = 0, FMT_BF16 = 1, FMT_I8 = 2, FMT_I4 = 3 };
+enum KvFmt { FMT_F32 = 0, FMT_BF16 = 1, FMT_I8 = 2, FMT_I4 = 3, FMT_F8 = 4 };
 
 template <int FMT> struct FmtBits;
 template <> struct FmtBits<FMT_F32> { static constexpr int v = 32; };
 template <> struct FmtBits<FMT_BF16> { static constexpr int v = 16; };
 template <> struct FmtBits<FMT_I8> { static constexpr int v = 8; };
 template <> struct FmtBits<FMT_I4> { static constexpr int v = 4; };
+template <> struct FmtBits<FMT_F8> { static constexpr int v = 8; };
+
+// Quantized formats: codes that share one fp16 scale per (block, KV head).
+template <int FMT> constexpr bool is_quant() { return FMT == FMT_I8 || FMT == FMT_I4 || FMT == FMT_F8; }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -64,6 +68,17 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 // Exact int8 -> bf16 of the four codes in a dword (|code| <= 128 fits bf16).
+// OCP fp8 e4m3 -> bf16 of the four bytes of a dword (byte 0 first, in the
+// low half of r[0]): two v_cvt_scalef32_pk_bf16_fp8 at scale 1. Every e4m3
+// value (3 mantissa bits, exponents 2^-9 .. 2^8) is a bf16 value, so the
+// conversion is exact.
+__device__ __forceinline__ u32x2 f8x4_to_bf16x4(uint32_t w) {
+    u32x2 r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+    return r;
+}
+
 __device__ __forceinline__ u32x2 i8x4_to_bf16x4(uint32_t w) {
     float f0 = (float)((int32_t)(w << 24) >> 24);
     float f1 = (float)((int32_t)(w << 16) >> 24);

@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p, int 
         if (key0 > wave_kmax) continue;  // every row of this wave is before this pair
 
         float ks0 = 1.f, ks1 = 1.f, vs0 = 1.f, vs1 = 1.f;
-        if (FMT == FMT_I8 || FMT == FMT_I4) {
+        if (is_quant<FMT>()) {
             ks0 = fp16_bits_to_f32(p.k_scales[(size_t)id0 * p.n_kv + kvh]);
             ks1 = fp16_bits_to_f32(p.k_scales[(size_t)id1 * p.n_kv + kvh]);
             vs0 = fp16_bits_to_f32(p.v_scales[(size_t)id0 * p.n_kv + kvh]);
