@@ -56,6 +56,12 @@ def test_host_sizes_match_formulas(B):
             assert L.pa_kv_cache_bytes(80, 8, 128, bits, n) == F.paged_cache_bytes(80, 8, 128, n, bits)
         assert L.pa_tile_bytes(128, bits) == 16 * 128 * bits // 8
     assert L.pa_tile_bytes(128, 12) == 0
+    # fp8 (e4m3): one byte per element plus the per-(block, head) scale, as int8
+    fp8 = B.PA_KV_FP8
+    assert L.pa_kv_bytes_per_token(80, 8, 128, fp8) * 2 == 327680
+    assert L.pa_tile_bytes(128, fp8) == L.pa_tile_bytes(128, 8) == 2048
+    for n in (0, 1, 17, 8000):
+        assert L.pa_kv_cache_bytes(80, 8, 128, fp8, n) == L.pa_kv_cache_bytes(80, 8, 128, 8, n)
 
 
 def _decode(B, **over):
@@ -73,6 +79,7 @@ def _decode(B, **over):
     (dict(mcl=-1), -1), (dict(pb=3), -1), (dict(pb=66), -1), (dict(dt=5), -1), (dict(bits=12), -1),
     (dict(d=96), -2), (dict(dt=0, bits=8), -2), (dict(dt=1, bits=32), -2), (dict(H=64, Hkv=2), -2),
     (dict(q=None), -1), (dict(out=None), -1), (dict(tables=None), -1), (dict(bits=8), -1),
+    (dict(bits=264), -1), (dict(dt=0, bits=264), -2),
     (dict(mcl=4096, ns=64, mb=256), -3),
 ])
 def test_decode_rejects_on_host(B, over, code):
@@ -128,3 +135,7 @@ def test_other_entry_points_reject_on_host(B):
     bad = list(args)
     bad[0] = None
     assert L.paged_attn_prefill_chunk(*bad) == -1
+    bad = list(args)
+    bad[19], bad[6], bad[7] = 264, one, one  # fp8 pools: decode only
+    assert L.paged_attn_prefill_chunk(*bad) == -2
+    assert L.kv_quantize(one, one, one, one, 0, 4, 2, 16, 128, 264, 0, None) == 0   # fp8 accepted
