@@ -282,6 +282,22 @@ int paged_kv_write(const void* k_src, const void* v_src, const int64_t* slot_map
                    void* k_pool, void* v_pool, int num_blocks, int block_size,
                    int n_kv_heads, int d_head, int dtype, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Copy whole blocks ([IR] "PagedAttention...": shared blocks are copied on
+ * write when sequences diverge; the host block manager of
+ * pa_block_manager.h reports the (source, destination) pairs).
+ * For each of the n_pairs pairs in `pairs` (device int32 [n_pairs][2]:
+ * source block, destination block), the block's tiles of every KV head are
+ * copied in k_pool and in v_pool (either may be NULL), and for quantized
+ * pools its fp16 scales in k_scales / v_scales (either may be NULL; both
+ * must be NULL for kv_bits 32 or 16). Pairs naming a block outside
+ * [0, num_blocks) are skipped. No destination may also appear as a source
+ * in the same call (the copies run in parallel).
+ * ------------------------------------------------------------------------ */
+int pa_copy_blocks(void* k_pool, void* v_pool, uint16_t* k_scales, uint16_t* v_scales,
+                   const int32_t* pairs, int n_pairs, int num_blocks, int n_kv_heads, int d_head,
+                   int kv_bits, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,11 +21,15 @@ PA_KIND_K, PA_KIND_V = 0, 1
 PA_KV_FP8 = 264  # kv_bits code of OCP fp8 e4m3 pools
 BLOCK_SIZE = 16
 
-# every function declared in include/paged_attn.h
+# every function declared in include/paged_attn.h and include/pa_block_manager.h
 EXPORTS = (
     "pa_error_string", "pa_tile_bytes", "pa_kv_bytes_per_token", "pa_kv_cache_bytes",
     "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_decode_window", "paged_attn_prefill_chunk",
-    "kv_quantize", "paged_kv_write",
+    "kv_quantize", "paged_kv_write", "pa_copy_blocks",
+    "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_ref_count", "pa_bm_add", "pa_bm_append",
+    "pa_bm_fork", "pa_bm_release", "pa_bm_num_tokens", "pa_bm_table",
+    "pa_sched_create", "pa_sched_destroy", "pa_sched_submit", "pa_sched_num_live", "pa_sched_step",
+    "pa_sched_record", "pa_sched_finish",
 )
 
 _lib = None
@@ -60,6 +64,43 @@ def _declare(lib):
     lib.kv_quantize.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
     lib.paged_kv_write.restype = i
     lib.paged_kv_write.argtypes = [vp, vp, vp, i, vp, vp, i, i, i, i, i, vp]
+    lib.pa_copy_blocks.restype = i
+    lib.pa_copy_blocks.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+    # host block manager and scheduler (opaque handles)
+    lib.pa_bm_create.restype = vp
+    lib.pa_bm_create.argtypes = [i, i]
+    lib.pa_bm_destroy.restype = None
+    lib.pa_bm_destroy.argtypes = [vp]
+    lib.pa_bm_num_free.restype = i
+    lib.pa_bm_num_free.argtypes = [vp]
+    lib.pa_bm_ref_count.restype = i
+    lib.pa_bm_ref_count.argtypes = [vp, i]
+    lib.pa_bm_add.restype = i
+    lib.pa_bm_add.argtypes = [vp, i64, vp, i, vp]
+    lib.pa_bm_append.restype = i
+    lib.pa_bm_append.argtypes = [vp, i64, vp, vp]
+    lib.pa_bm_fork.restype = i
+    lib.pa_bm_fork.argtypes = [vp, i64, i64]
+    lib.pa_bm_release.restype = i
+    lib.pa_bm_release.argtypes = [vp, i64]
+    lib.pa_bm_num_tokens.restype = i
+    lib.pa_bm_num_tokens.argtypes = [vp, i64]
+    lib.pa_bm_table.restype = i
+    lib.pa_bm_table.argtypes = [vp, i64, vp, i]
+    lib.pa_sched_create.restype = vp
+    lib.pa_sched_create.argtypes = [vp]
+    lib.pa_sched_destroy.restype = None
+    lib.pa_sched_destroy.argtypes = [vp]
+    lib.pa_sched_submit.restype = i
+    lib.pa_sched_submit.argtypes = [vp, i64, vp, i]
+    lib.pa_sched_num_live.restype = i
+    lib.pa_sched_num_live.argtypes = [vp]
+    lib.pa_sched_step.restype = i
+    lib.pa_sched_step.argtypes = [vp, i, vp, vp, vp, vp, vp, vp, vp]
+    lib.pa_sched_record.restype = i
+    lib.pa_sched_record.argtypes = [vp, i64, i64]
+    lib.pa_sched_finish.restype = i
+    lib.pa_sched_finish.argtypes = [vp, i64]
 
 
 def lib():
@@ -245,3 +286,115 @@ def kv_write(k_src, v_src, slot_mapping, k_pool, v_pool, *, n_kv_heads, stream=N
     st = lib().paged_kv_write(_p(k_src), _p(v_src), _p(slot_mapping), T, _p(k_pool), _p(v_pool), nb, BLOCK_SIZE,
                               n_kv_heads, D, dt, _stream(stream, dev))
     _check("paged_kv_write", st)
+
+
+def copy_blocks(pairs, k_pool, v_pool, *, n_kv_heads, d_head, kv_bits, k_scales=None, v_scales=None, stream=None):
+    """pa_copy_blocks: pairs int32 [n, 2] (source, destination) on the pools' device."""
+    dev = _gpu(pairs, k_pool, v_pool, k_scales, v_scales)
+    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2 or not pairs.is_contiguous():
+        raise PagedAttnError("pairs must be a contiguous int32 [n, 2] tensor")
+    nb = _num_blocks(k_pool if k_pool is not None else v_pool, n_kv_heads, d_head, kv_bits)
+    st = lib().pa_copy_blocks(_p(k_pool), _p(v_pool), _p(k_scales), _p(v_scales), _p(pairs), int(pairs.shape[0]),
+                              nb, n_kv_heads, d_head, kv_bits, _stream(stream, dev))
+    _check("pa_copy_blocks", st)
+
+
+class BlockManager:
+    """The library's host block manager (include/pa_block_manager.h)."""
+
+    def __init__(self, num_blocks: int, prefix_cache: bool = True):
+        self._h = lib().pa_bm_create(int(num_blocks), int(bool(prefix_cache)))
+        if not self._h:
+            raise PagedAttnError("pa_bm_create failed")
+
+    def close(self):
+        if self._h:
+            lib().pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def handle(self):
+        return self._h
+
+    def num_free(self) -> int:
+        return lib().pa_bm_num_free(self._h)
+
+    def ref_count(self, block: int) -> int:
+        return lib().pa_bm_ref_count(self._h, int(block))
+
+    def add(self, seq: int, tokens) -> int:
+        arr = (ctypes.c_int64 * len(tokens))(*[int(t) for t in tokens])
+        cached = ctypes.c_int(0)
+        _check("pa_bm_add", lib().pa_bm_add(self._h, int(seq), arr, len(tokens), ctypes.byref(cached)))
+        return cached.value
+
+    def append(self, seq: int):
+        src, dst = ctypes.c_int32(-1), ctypes.c_int32(-1)
+        _check("pa_bm_append", lib().pa_bm_append(self._h, int(seq), ctypes.byref(src), ctypes.byref(dst)))
+        return None if src.value < 0 else (src.value, dst.value)
+
+    def fork(self, parent: int, child: int) -> None:
+        _check("pa_bm_fork", lib().pa_bm_fork(self._h, int(parent), int(child)))
+
+    def release(self, seq: int) -> None:
+        _check("pa_bm_release", lib().pa_bm_release(self._h, int(seq)))
+
+    def num_tokens(self, seq: int) -> int:
+        n = lib().pa_bm_num_tokens(self._h, int(seq))
+        _check("pa_bm_num_tokens", min(n, 0))
+        return n
+
+    def table(self, seq: int):
+        n = lib().pa_bm_table(self._h, int(seq), None, 0)
+        _check("pa_bm_table", min(n, 0))
+        row = (ctypes.c_int32 * max(n, 1))()
+        lib().pa_bm_table(self._h, int(seq), row, n)
+        return list(row[:n])
+
+
+class Scheduler:
+    """The library's scheduler step over a BlockManager."""
+
+    def __init__(self, bm: BlockManager):
+        self.bm = bm
+        self._h = lib().pa_sched_create(bm.handle)
+        if not self._h:
+            raise PagedAttnError("pa_sched_create failed")
+
+    def close(self):
+        if self._h:
+            lib().pa_sched_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def submit(self, seq: int, prompt) -> None:
+        arr = (ctypes.c_int64 * len(prompt))(*[int(t) for t in prompt])
+        _check("pa_sched_submit", lib().pa_sched_submit(self._h, int(seq), arr, len(prompt)))
+
+    def step(self):
+        """(running, preempted, cow pairs, stalled count)."""
+        cap = max(1, lib().pa_sched_num_live(self._h))
+        run, pre = (ctypes.c_int64 * cap)(), (ctypes.c_int64 * cap)()
+        cow = (ctypes.c_int32 * (2 * cap))()
+        nr, npre, nc, ns = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        _check("pa_sched_step", lib().pa_sched_step(self._h, cap, run, ctypes.byref(nr), pre, ctypes.byref(npre),
+                                                    cow, ctypes.byref(nc), ctypes.byref(ns)))
+        pairs = [(cow[2 * i], cow[2 * i + 1]) for i in range(nc.value)]
+        return list(run[:nr.value]), list(pre[:npre.value]), pairs, ns.value
+
+    def record(self, seq: int, token: int) -> None:
+        _check("pa_sched_record", lib().pa_sched_record(self._h, int(seq), int(token)))
+
+    def finish(self, seq: int) -> None:
+        _check("pa_sched_finish", lib().pa_sched_finish(self._h, int(seq)))

@@ -100,6 +100,8 @@ const char* pa_error_string(int status) {
         case PA_ERR_UNSUPPORTED: return "unsupported shape or format";
         case PA_ERR_WORKSPACE: return "workspace missing or too small";
         case PA_ERR_HIP: return "HIP runtime error";
+        case -5: return "not enough free KV blocks";
+        case -6: return "unknown (or already used) sequence id";
         default: return "unknown status";
     }
 }
@@ -327,6 +329,20 @@ int kv_quantize(const void* src, void* codes, uint16_t* scales, const int32_t* b
     // the kernels take 0 for fp8 codes
     const hipError_t e = pa::launch_quantize(src, codes, scales, block_ids, n, num_blocks, n_kv_heads, d_head,
                                              bits == PA_KV_FP8 ? 0 : bits, kind, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int pa_copy_blocks(void* k_pool, void* v_pool, uint16_t* k_scales, uint16_t* v_scales, const int32_t* pairs,
+                   int n_pairs, int num_blocks, int n_kv_heads, int d_head, int kv_bits, void* stream) {
+    if (n_pairs < 0 || num_blocks <= 0 || n_kv_heads <= 0 || d_head <= 0 || !valid_kv_bits(kv_bits))
+        return PA_ERR_INVALID_ARG;
+    if (d_head != 64 && d_head != 128) return PA_ERR_UNSUPPORTED;
+    if (n_pairs == 0) return PA_OK;
+    if (!pairs || n_pairs > 0x7fffffff) return PA_ERR_INVALID_ARG;
+    if (!quantized(kv_bits) && (k_scales || v_scales)) return PA_ERR_INVALID_ARG;
+    const size_t block_bytes = (size_t)n_kv_heads * PA_BLOCK_SIZE * d_head * storage_bits(kv_bits) / 8;
+    const hipError_t e = pa::launch_copy_blocks(k_pool, v_pool, k_scales, v_scales, pairs, n_pairs, num_blocks,
+                                                n_kv_heads, block_bytes, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

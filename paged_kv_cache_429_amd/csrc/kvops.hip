@@ -201,3 +201,46 @@ hipError_t launch_kv_write(const void* k_src, const void* v_src, const int64_t* 
 }
 
 }  // namespace pa
+
+namespace pa {
+
+// Copy-on-write block copies: workgroup i copies the n_kv tiles of block
+// pairs[2i] to block pairs[2i+1] in both pools (bytes = n_kv * tile bytes,
+// a multiple of 16) and, when given, the blocks' scales. Pairs naming a
+// block outside [0, num_blocks) are skipped.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ kpool, uint8_t* __restrict__ vpool,
+                                                         uint16_t* __restrict__ kscales,
+                                                         uint16_t* __restrict__ vscales,
+                                                         const int32_t* __restrict__ pairs, int num_blocks,
+                                                         int n_kv, size_t block_bytes) {
+    const int src = pairs[2 * blockIdx.x];
+    const int dst = pairs[2 * blockIdx.x + 1];
+    if ((unsigned)src >= (unsigned)num_blocks || (unsigned)dst >= (unsigned)num_blocks) return;
+    const size_t n16 = block_bytes / 16;
+    for (size_t i = threadIdx.x; i < n16; i += 256) {
+        if (kpool) {
+            reinterpret_cast<u32x4*>(kpool + (size_t)dst * block_bytes)[i] =
+                reinterpret_cast<const u32x4*>(kpool + (size_t)src * block_bytes)[i];
+        }
+        if (vpool) {
+            reinterpret_cast<u32x4*>(vpool + (size_t)dst * block_bytes)[i] =
+                reinterpret_cast<const u32x4*>(vpool + (size_t)src * block_bytes)[i];
+        }
+    }
+    for (int h = threadIdx.x; h < n_kv; h += 256) {
+        if (kscales) kscales[(size_t)dst * n_kv + h] = kscales[(size_t)src * n_kv + h];
+        if (vscales) vscales[(size_t)dst * n_kv + h] = vscales[(size_t)src * n_kv + h];
+    }
+}
+
+hipError_t launch_copy_blocks(void* k_pool, void* v_pool, uint16_t* k_scales, uint16_t* v_scales,
+                              const int32_t* pairs, int n_pairs, int num_blocks, int n_kv, size_t block_bytes,
+                              hipStream_t stream) {
+    if (n_pairs == 0) return hipSuccess;
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)n_pairs), dim3(256), 0, stream,
+                       static_cast<uint8_t*>(k_pool), static_cast<uint8_t*>(v_pool), k_scales, v_scales, pairs,
+                       num_blocks, n_kv, block_bytes);
+    return hipGetLastError();
+}
+
+}  // namespace pa

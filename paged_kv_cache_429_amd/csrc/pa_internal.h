@@ -130,6 +130,10 @@ hipError_t launch_prefix(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_quantize(const void* src, void* codes, uint16_t* scales, const int32_t* block_ids, int n_ids,
                            int num_blocks, int n_kv, int d, int bits, int kind, hipStream_t stream);
 
+hipError_t launch_copy_blocks(void* k_pool, void* v_pool, uint16_t* k_scales, uint16_t* v_scales,
+                              const int32_t* pairs, int n_pairs, int num_blocks, int n_kv, size_t block_bytes,
+                              hipStream_t stream);
+
 hipError_t launch_kv_write(const void* k_src, const void* v_src, const int64_t* slots, int num_tokens,
                            void* k_pool, void* v_pool, int num_blocks, int n_kv, int d, int fmt,
                            hipStream_t stream);

@@ -12,7 +12,7 @@ import pytest
 from oracle import formulas as F
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("paged_attn.h", "pa_block_manager.h")]
 
 
 @pytest.fixture(scope="module")
@@ -25,7 +25,7 @@ def B():
 
 
 def header_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\([^;{}]*\)\s*;", text)))
 
