@@ -183,20 +183,12 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool, const uin
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d_head));
     p.window = window;
 
-    // Shared-prefix workgroups (groups of 16/G consecutive sequences whose
-    // tables name the same blocks fill the 16 MFMA columns) for the MFMA
-    // formats at G = 4 or 8, when sequences can be split.
+    // Shared-prefix groups (16/G consecutive sequences whose tables name the
+    // same blocks fill the 16 MFMA columns, computed by the workgroup of the
+    // group's first sequence) for the MFMA formats at G = 4 or 8, when
+    // sequences can be split and the batch holds a whole group.
     p.share_n = 0;
-    p.n_shared = 0;
-    if (fmt != 0 && p.pmax > 1 && window == 0) {
-        p.share_n = (G == 4 || G == 8) ? 16 / G : 0;
-        if (p.share_n > 0) {
-            const long n = (long)(num_seqs / p.share_n) * p.pmax * n_kv_heads;
-            if (n > 0x3fffffffL) return PA_ERR_UNSUPPORTED;
-            p.n_shared = (int)n;
-            if (p.n_shared == 0) p.share_n = 0;
-        }
-    }
+    if (fmt != 0 && p.pmax > 1 && window == 0 && (G == 4 || G == 8) && num_seqs >= 16 / G) p.share_n = 16 / G;
     // Prefix pass (bf16 pools): a launch before the decode that attends each
     // tile's common leading run of blocks for all its rows at once.
     p.kpmax = fmt == 1 && window == 0 ? plan_prefix_parts(num_seqs, n_heads, n_kv_heads, d_head, p.ctx_cap, p.pmax)

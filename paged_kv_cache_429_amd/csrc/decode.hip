@@ -57,18 +57,8 @@ void decode_kernel(DecodeParams p) {
     WaveState<D>& st = *reinterpret_cast<WaveState<D>*>(smem);
     float* const scratch = reinterpret_cast<float*>(smem);
     constexpr bool F32OUT = (FMT == FMT_F32);
-    if constexpr (FMT != FMT_F32) {
-        if ((int)blockIdx.x < p.n_shared) {
-            if (p.share_n == 2) {
-                shared_unit<D, FMT, 1, 2, F32OUT>(p, blockIdx.x, st, scratch, kCap);
-            } else {
-                shared_unit<D, FMT, 1, 4, F32OUT>(p, blockIdx.x, st, scratch, kCap);
-            }
-            return;
-        }
-    }
     Unit u;
-    const int unit = blockIdx.x - p.n_shared;
+    const int unit = blockIdx.x;
     u.kvh = unit % p.n_kv;
     const int rest = unit / p.n_kv;
     // Highest partitions first, partition 0 of every sequence last: the
@@ -84,6 +74,19 @@ void decode_kernel(DecodeParams p) {
     } else {
         u.s = rest % p.num_seqs;
         u.part = p.pmax - 1 - rest / p.num_seqs;
+    }
+    // Without a prefix pass or a window the partition starts at block
+    // part * pb whatever the length, so its block ids are fetched together
+    // with the length (entries past the sequence's end are never used)
+    // instead of one memory round trip later.
+    const int32_t* trow = p.tables + (size_t)u.s * p.max_blocks;
+    const bool ids_early = FMT != FMT_F32 && p.prefix_ts == 0 && p.window == 0;
+    int id_lo = 0, id_hi = 0;
+    if (ids_early) {
+        const int first = u.part * p.pb;  // < blocks of a sequence at ctx_cap <= max_blocks
+        const int avail = p.max_blocks - first;
+        id_lo = load_ids(trow, first, min(avail, 64), p.num_blocks);
+        id_hi = avail > 64 ? load_ids(trow, first + 64, min(avail - 64, 64), p.num_blocks) : 0;
     }
     u.ctx = min(p.ctx[u.s], p.ctx_cap);
     if (u.ctx <= 0) {
@@ -105,12 +108,27 @@ void decode_kernel(DecodeParams p) {
     if (u.part >= u.nparts) return;
     u.b_begin = b0 + u.part * p.pb;
     u.b_end = b0 + part_end(u.nblk - b0, p.pb, u.part, u.nparts);
-    if (p.share_n > 0 && b0 == 0) {  // taken by a shared-prefix workgroup?
-        const int grp = u.s / p.share_n;
-        if ((grp + 1) * p.share_n <= p.num_seqs && group_shares(p, grp * p.share_n, u.part)) return;
+    if constexpr (FMT != FMT_F32) {
+        // A group of share_n sequences that shares this partition's first
+        // pair is computed by the workgroup of its first sequence, for all
+        // of them; the others' workgroups have nothing to do.
+        if (p.share_n > 0 && b0 == 0) {
+            const int grp = u.s / p.share_n;
+            const int s0 = grp * p.share_n;
+            if (s0 + p.share_n <= p.num_seqs && group_shares(p, s0, u.part)) {
+                if (u.s == s0) {
+                    const int gunit = (grp * p.pmax + u.part) * p.n_kv + u.kvh;
+                    if (p.share_n == 2) {
+                        shared_unit<D, FMT, 1, 2, F32OUT>(p, gunit, st, scratch, kCap);
+                    } else {
+                        shared_unit<D, FMT, 1, 4, F32OUT>(p, gunit, st, scratch, kCap);
+                    }
+                }
+                return;
+            }
+        }
     }
 
-    const int32_t* trow = p.tables + (size_t)u.s * p.max_blocks;
     if constexpr (FMT == FMT_F32) {
         __shared__ float qs[16 * D];
         const float* qg = reinterpret_cast<const float*>(p.q) + ((size_t)u.s * p.n_heads + u.kvh * p.group) * D;
@@ -118,9 +136,11 @@ void decode_kernel(DecodeParams p) {
         __syncthreads();
         f32_wave<D>(p, u, trow, st, qs);
     } else {
-        const int nbp = u.b_end - u.b_begin;
-        const int id_lo = load_ids(trow, u.b_begin, min(nbp, 64), p.num_blocks);
-        const int id_hi = nbp > 64 ? load_ids(trow, u.b_begin + 64, nbp - 64, p.num_blocks) : 0;
+        if (!ids_early) {
+            const int nbp = u.b_end - u.b_begin;
+            id_lo = load_ids(trow, u.b_begin, min(nbp, 64), p.num_blocks);
+            id_hi = nbp > 64 ? load_ids(trow, u.b_begin + 64, nbp - 64, p.num_blocks) : 0;
+        }
         mfma_wave<D, FMT>(p, u, id_lo, id_hi, st);
     }
     epilogue<D, F32OUT>(p, u, st, scratch, kCap);
@@ -158,7 +178,7 @@ void decode_workspace_carve(void* ws, int num_seqs, int n_heads, int n_kv, int d
 
 template <int D, int FMT>
 static hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
-    const size_t grid = (size_t)p.n_shared + (size_t)p.num_seqs * p.pmax * p.n_kv;
+    const size_t grid = (size_t)p.num_seqs * p.pmax * p.n_kv;
     if (grid == 0) return hipSuccess;
     if (grid > 0x7fffffffu) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((decode_kernel<D, FMT>), dim3((unsigned)grid), dim3(kThreads), 0, stream, p);

@@ -1120,7 +1120,8 @@ __device__ __forceinline__ void epilogue(const DecodeParams& p, const Unit& u, W
 //
 // A group of NS = 16/G consecutive sequences (G = 4 or 8) whose tables name
 // the same physical blocks for the first pair of a partition, all full, is
-// processed by one workgroup for that (KV head, partition): the G query
+// processed for that (KV head, partition) by the workgroup of the group's
+// first sequence, the others' workgroups returning at once: the G query
 // heads of the NS sequences fill the 16 MFMA columns (one column set per
 // wave). A block pair that every sequence
 // of the group shares (same ids, full in every sequence) is loaded once, with

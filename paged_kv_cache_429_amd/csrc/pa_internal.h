@@ -69,8 +69,7 @@ struct DecodeParams {
     int pmax;           // num_parts() of a sequence at max_context_len
     int pb;             // blocks per partition (even)
     float scale_log2;   // log2(e) / sqrt(d)
-    int share_n;        // sequences per shared-prefix group (0: no shared-prefix workgroups)
-    int n_shared;       // shared-prefix workgroups, first in the grid: (S / share_n) * pmax * n_kv
+    int share_n;        // sequences per shared-prefix group (0: no group check)
     int pslots;         // partial slots per (sequence, query head): kpmax + pmax
     int prefix_ts;      // sequences per prefix-pass tile (0: no prefix pass)
     int kpmax;          // prefix partitions per tile at most
