@@ -15,6 +15,10 @@ Timing: after the warm-up, K steps run back to back for the wall-clock
 value, then the same K steps again, each bracketed by HIP events on its
 stream, for the kernel time of the roofline.
 
+The line also carries the device's measured read ceiling (the library's
+read probe: random 4 KiB tiles, and a stream) and the decode's fraction of
+it, beside the fraction of the 8 TB/s spec peak.
+
 The line printed carries the achieved HBM bandwidth over algorithmic bytes
 (K/V of every attended token once per KV head, plus Q, O, the table entries
 and lengths read), the decode tokens/s per layer, a roofline object for the
@@ -61,6 +65,8 @@ def parse():
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window in tokens for the decode workloads (0: full attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip measuring the device's read ceiling (random 4 KiB tiles and a stream)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device copy of this many MiB (calibrates "
@@ -126,6 +132,35 @@ PA_KV_FP8 = 264  # kv_bits code of fp8 (e4m3) pools in the library's ABI
 
 def storage_bits(kv_bits):
     return 8 if kv_bits == PA_KV_FP8 else kv_bits
+
+
+def read_ceiling(torch, B, gib=4, reps=10):
+    """The device's measured read bandwidth on the decode's access pattern:
+    the library's read probe over a `gib` GiB buffer, once as 4 KiB tiles in
+    a random order (one (block, KV head) bf16 tile at d_head 128) and once as
+    a stream; GB/s from HIP events around `reps` passes after two warm-ups."""
+    tile = 4096
+    n = (gib << 30) // tile
+    buf = torch.empty(n * tile, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    g = torch.Generator(device="cpu").manual_seed(4290)
+    order = torch.randperm(n, generator=g).to(torch.int32).cuda()
+    grid = 16384  # many more workgroups than resident slots: no idle CUs at the end of a pass
+    xo = torch.empty(grid, dtype=torch.int32, device="cuda")
+    out = {}
+    for name, o in (("random_4k_tiles_GBps", order), ("stream_GBps", None)):
+        for _ in range(2):
+            B.hbm_read_probe(buf, tile, order=o, grid=grid, xor_out=xo)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            B.hbm_read_probe(buf, tile, order=o, grid=grid, xor_out=xo)
+        e.record()
+        torch.cuda.synchronize()
+        out[name] = round(n * tile * reps / (s.elapsed_time(e) * 1e-3) / 1e9, 1)
+    del buf, order
+    out.update({"buffer_bytes": n * tile, "reps": reps, "loads": "16-byte nontemporal", "workgroups": grid})
+    return out
 
 
 def decode_bytes(case, kv_bits, window=0):
@@ -465,6 +500,11 @@ def main():
         },
         "input_generation_s": round(gen_s, 2),
     }
+    if not a.no_read_probe:
+        # the same box's measured read ceiling, beside the spec peak
+        rc = read_ceiling(torch, B)
+        res["measured_read"] = rc
+        res["roofline"]["frac_of_measured_random_tiles"] = round(achieved / rc["random_4k_tiles_GBps"], 4)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, kv_bits, a.cpu_seconds, a.window)
     print(json.dumps(res), flush=True)

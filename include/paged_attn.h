@@ -298,6 +298,22 @@ int pa_copy_blocks(void* k_pool, void* v_pool, uint16_t* k_scales, uint16_t* v_s
                    const int32_t* pairs, int n_pairs, int num_blocks, int n_kv_heads, int d_head,
                    int kv_bits, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * HBM read probe: the read bandwidth this device reaches on the decode's
+ * access pattern, the measured ceiling that the decode's bandwidth is
+ * reported against beside the spec peak ([JE] "KV-cache quantization":
+ * decode is bound by the bytes moved per step). buf holds buf_bytes / tile_bytes
+ * tiles of tile_bytes (a multiple of 16, at most 65536). The tiles read are
+ * order[0 .. n_order) (device int32 tile numbers; entries outside the
+ * buffer are skipped), or with order NULL every tile of buf in turn.
+ * Workgroup w of the grid (1..65536 workgroups of 256 threads) reads the
+ * w-th, (w + grid)-th, (w + 2 grid)-th, ... of them with nontemporal
+ * 16-byte loads and writes the XOR of every 32-bit word it read to
+ * xor_out[w] (device uint32 [grid]). Nothing else is written.
+ * ------------------------------------------------------------------------ */
+int pa_hbm_read_probe(const void* buf, int64_t buf_bytes, int tile_bytes, const int32_t* order, int64_t n_order,
+                      uint32_t* xor_out, int grid, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ BLOCK_SIZE = 16
 EXPORTS = (
     "pa_error_string", "pa_tile_bytes", "pa_kv_bytes_per_token", "pa_kv_cache_bytes",
     "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_decode_window", "paged_attn_prefill_chunk",
-    "kv_quantize", "paged_kv_write", "pa_copy_blocks",
+    "kv_quantize", "paged_kv_write", "pa_copy_blocks", "pa_hbm_read_probe",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_ref_count", "pa_bm_add", "pa_bm_append",
     "pa_bm_fork", "pa_bm_release", "pa_bm_num_tokens", "pa_bm_table",
     "pa_sched_create", "pa_sched_destroy", "pa_sched_submit", "pa_sched_num_live", "pa_sched_step",
@@ -66,6 +66,8 @@ def _declare(lib):
     lib.paged_kv_write.argtypes = [vp, vp, vp, i, vp, vp, i, i, i, i, i, vp]
     lib.pa_copy_blocks.restype = i
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.pa_hbm_read_probe.restype = i
+    lib.pa_hbm_read_probe.argtypes = [vp, i64, i, vp, i64, vp, i, vp]
     # host block manager and scheduler (opaque handles)
     lib.pa_bm_create.restype = vp
     lib.pa_bm_create.argtypes = [i, i]
@@ -297,6 +299,20 @@ def copy_blocks(pairs, k_pool, v_pool, *, n_kv_heads, d_head, kv_bits, k_scales=
     st = lib().pa_copy_blocks(_p(k_pool), _p(v_pool), _p(k_scales), _p(v_scales), _p(pairs), int(pairs.shape[0]),
                               nb, n_kv_heads, d_head, kv_bits, _stream(stream, dev))
     _check("pa_copy_blocks", st)
+
+
+def hbm_read_probe(buf, tile_bytes, *, order=None, grid=2048, xor_out=None, stream=None):
+    """pa_hbm_read_probe over a uint8 device buffer cut into tiles of
+    tile_bytes; returns the per-workgroup XOR words (int32 [grid])."""
+    dev = _gpu(buf, order, xor_out)
+    if order is not None and order.dtype != torch.int32:
+        raise PagedAttnError("order must be int32")
+    if xor_out is None:
+        xor_out = torch.empty(grid, dtype=torch.int32, device=dev)
+    st = lib().pa_hbm_read_probe(_p(buf), buf.numel(), tile_bytes, _p(order), 0 if order is None else order.numel(),
+                                 _p(xor_out), grid, _stream(stream, dev))
+    _check("pa_hbm_read_probe", st)
+    return xor_out
 
 
 class BlockManager:

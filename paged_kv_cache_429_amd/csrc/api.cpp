@@ -338,6 +338,19 @@ int pa_copy_blocks(void* k_pool, void* v_pool, uint16_t* k_scales, uint16_t* v_s
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+int pa_hbm_read_probe(const void* buf, int64_t buf_bytes, int tile_bytes, const int32_t* order, int64_t n_order,
+                      uint32_t* xor_out, int grid, void* stream) {
+    if (buf_bytes < 0 || n_order < 0 || tile_bytes < 16 || tile_bytes > 65536 || tile_bytes % 16 != 0)
+        return PA_ERR_INVALID_ARG;
+    if (grid <= 0 || grid > 65536 || !xor_out || (buf_bytes > 0 && !buf) || (n_order > 0 && !order))
+        return PA_ERR_INVALID_ARG;
+    const long buf_tiles = (long)(buf_bytes / tile_bytes);
+    const long n_tiles = order ? (long)n_order : buf_tiles;
+    const hipError_t e = pa::launch_read_probe(buf, buf_tiles, n_tiles, tile_bytes, order, xor_out, grid,
+                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 int paged_kv_write(const void* k_src, const void* v_src, const int64_t* slot_mapping, int num_tokens,
                    void* k_pool, void* v_pool, int num_blocks, int block_size,
                    int n_kv_heads, int d_head, int dtype, void* stream) {

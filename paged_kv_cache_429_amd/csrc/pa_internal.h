@@ -133,6 +133,9 @@ hipError_t launch_copy_blocks(void* k_pool, void* v_pool, uint16_t* k_scales, ui
                               const int32_t* pairs, int n_pairs, int num_blocks, int n_kv, size_t block_bytes,
                               hipStream_t stream);
 
+hipError_t launch_read_probe(const void* buf, long buf_tiles, long n_tiles, int tile_bytes, const int32_t* order,
+                             uint32_t* xor_out, int grid, hipStream_t stream);
+
 hipError_t launch_kv_write(const void* k_src, const void* v_src, const int64_t* slots, int num_tokens,
                            void* k_pool, void* v_pool, int num_blocks, int n_kv, int d, int fmt,
                            hipStream_t stream);

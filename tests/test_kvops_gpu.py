@@ -172,3 +172,27 @@ def test_quantized_retrieval_probe_exact(lib, bits, d):
         sl = c.block_tables[s, t // 16] * 16 + t % 16
         for h in range(16):
             assert np.array_equal(got[s, h], v[sl, h // 4]), (bits, s, h, got[s, h][:8], v[sl, h // 4][:8])
+
+
+@pytest.mark.parametrize("tile_bytes,grid,ordered", [(4096, 64, True), (4096, 7, False), (1024, 300, True),
+                                                     (16, 3, True), (65536, 5, False)])
+def test_hbm_read_probe_reads_every_listed_tile(lib, tile_bytes, grid, ordered):
+    """The read probe's per-workgroup XOR equals the XOR of the tiles that
+    workgroup is assigned (w, w + grid, ...), so every listed tile is read
+    whole; order entries outside the buffer are skipped."""
+    g = np.random.default_rng(tile_bytes + grid)
+    n_buf = max(8, (1 << 22) // tile_bytes)
+    host = g.integers(0, 256, n_buf * tile_bytes, dtype=np.uint8)
+    buf = torch.from_numpy(host).cuda()
+    order = None
+    tiles = np.arange(n_buf)
+    if ordered:
+        tiles = np.concatenate([g.permutation(n_buf), [-1, n_buf, n_buf + 7], g.integers(0, n_buf, 50)]).astype(np.int32)
+        order = torch.from_numpy(tiles).cuda()
+    got = B.hbm_read_probe(buf, tile_bytes, order=order, grid=grid).cpu().numpy().view(np.uint32)
+    tile_xor = np.bitwise_xor.reduce(host.view(np.uint32).reshape(n_buf, tile_bytes // 4), axis=1)
+    want = np.zeros(grid, dtype=np.uint32)
+    for t, tid in enumerate(tiles):
+        if 0 <= tid < n_buf:
+            want[t % grid] ^= tile_xor[tid]
+    assert np.array_equal(got, want)
