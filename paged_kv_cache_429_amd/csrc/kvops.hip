@@ -244,3 +244,53 @@ hipError_t launch_copy_blocks(void* k_pool, void* v_pool, uint16_t* k_scales, ui
 }
 
 }  // namespace pa
+
+namespace pa {
+
+// Read-bandwidth probe: workgroup w reads tiles w, w + grid, w + 2 grid, ...
+// of n_tiles (tile t at byte offset (order ? order[t] : t) * tile_bytes,
+// skipped unless that tile lies in the buf_tiles of the buffer; 16-byte
+// nontemporal loads, kProbeDepth tiles in flight per thread) and writes the
+// XOR of every 32-bit word it read to xor_out[w].
+constexpr int kProbeDepth = 8;
+
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint8_t* __restrict__ buf, long buf_tiles,
+                                                        long n_tiles, int tile_bytes,
+                                                        const int32_t* __restrict__ order,
+                                                        uint32_t* __restrict__ xor_out) {
+    const int per_tile = tile_bytes / 16;  // 16-byte pieces per tile
+    uint32_t acc = 0;
+    const long stride = gridDim.x;
+    for (long t0 = blockIdx.x; t0 < n_tiles; t0 += stride * kProbeDepth) {
+        for (int e = threadIdx.x; e < per_tile; e += 256) {
+            u32x4 v[kProbeDepth];
+#pragma unroll
+            for (int k = 0; k < kProbeDepth; ++k) {
+                const long t = t0 + k * stride;
+                v[k] = u32x4{0u, 0u, 0u, 0u};
+                const long tile = t < n_tiles ? (order ? (long)order[t] : t) : -1;
+                if (tile >= 0 && tile < buf_tiles) {
+                    v[k] = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x4*>(buf + tile * (long)tile_bytes) + e);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kProbeDepth; ++k) acc ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
+        }
+    }
+    __shared__ uint32_t red[4];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc ^= __shfl_xor(acc, m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) xor_out[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+hipError_t launch_read_probe(const void* buf, long buf_tiles, long n_tiles, int tile_bytes, const int32_t* order,
+                             uint32_t* xor_out, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       static_cast<const uint8_t*>(buf), buf_tiles, n_tiles, tile_bytes, order, xor_out);
+    return hipGetLastError();
+}
+
+}  // namespace pa
