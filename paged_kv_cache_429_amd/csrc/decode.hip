@@ -64,13 +64,14 @@ void decode_kernel(DecodeParams p) {
     // Highest partitions first, partition 0 of every sequence last: the
     // last round of workgroups then holds whole short sequences and full
     // first partitions, of similar size, instead of a random mix (the
-    // order changes nothing but when a unit runs). With the prefix pass a
-    // sequence's partitions are consecutive instead, so that the units left
-    // without blocks (the run shortened the sequence) are spread over the
-    // launch rather than bunched at its start.
+    // order changes nothing but when a unit runs). With the prefix pass,
+    // partition 0 of every sequence comes first instead: the run usually
+    // leaves a sequence one short partition, so the units left without
+    // blocks fall at the end of the launch, where they exit while the last
+    // real units run.
     if (p.prefix_ts > 0) {
-        u.s = rest / p.pmax;
-        u.part = rest % p.pmax;
+        u.s = rest % p.num_seqs;
+        u.part = rest / p.num_seqs;
     } else {
         u.s = rest % p.num_seqs;
         u.part = p.pmax - 1 - rest / p.num_seqs;
