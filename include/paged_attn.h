@@ -178,12 +178,13 @@ uint64_t pa_kv_cache_bytes(int n_layers, int n_kv_heads, int d_head, int kv_bits
  *                with the decode's partitions of the blocks after the run.
  *                Such sequences agree with private copies of the same
  *                blocks to rounding, not bit for bit.
- *              - Shared workgroups. Elsewhere, consecutive sequences (16 / G
+ *              - Shared groups. Elsewhere, consecutive sequences (16 / G
  *                of them, for G = 4 or 8) whose tables name the same
  *                physical blocks for a partition's first two blocks are
- *                processed together, each shared block being read once for
- *                the group; results are bit-identical to those of private
- *                copies of the same blocks.
+ *                processed together, by the workgroup of the group's first
+ *                sequence, each shared block being read once for the group;
+ *                results are bit-identical to those of private copies of
+ *                the same blocks.
  * ------------------------------------------------------------------------ */
 size_t paged_attn_decode_workspace_size(int num_seqs, int n_heads, int n_kv_heads, int d_head,
                                         int max_context_len, int partition_blocks);
