@@ -282,6 +282,30 @@ def test_retrieval_probe_exact(lib, dtype, d, pb):
             assert np.array_equal(got[s, h], v[slot, h // 4]), (s, h, got[s, h][:4], v[slot, h // 4][:4])
 
 
+@pytest.mark.parametrize("dtype,pb", [("f32", 0), ("bf16", 0), ("bf16", 2)])
+def test_retrieval_probe_negative_control(lib, dtype, pb):
+    """A corrupted (but in-range) block-table entry must fail the probe: the
+    sequence whose magnet block is replaced by another sequence's block no
+    longer returns V at its magnet, and the GPU agrees with the oracle on the
+    corrupted table; the other sequences stay exact."""
+    c = make_probe_case(16, 4, 128, dtype, [1000, 999, 600], 306)
+    t = int(c.extra["tstar"][0])
+    good_slot = c.block_tables[0, t // 16] * 16 + t % 16
+    v = oracle.as_f64(c.v_slots, dtype)
+    # sequence 0's magnet block now points at sequence 2's block of the same logical index
+    j = t // 16
+    c.block_tables[0, j] = c.block_tables[2, min(j, (600 - 1) // 16)]
+    got = dev_to_f64(gpu_decode(c, partition_blocks=pb))
+    for h in range(16):
+        assert not np.array_equal(got[0, h], v[good_slot, h // 4])
+    assert_close(got, oracle_decode(c), dtype, "corrupted table")
+    for s in (1, 2):
+        ts = int(c.extra["tstar"][s])
+        slot = c.block_tables[s, ts // 16] * 16 + ts % 16
+        for h in range(16):
+            assert np.array_equal(got[s, h], v[slot, h // 4])
+
+
 def test_zero_and_clamped_contexts(lib):
     c = make_decode_case(8, 2, 128, "bf16", [40, 40, 40], 304, pool_factor=1.2)
     c.context_lens[1] = 0
