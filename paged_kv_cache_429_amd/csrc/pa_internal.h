@@ -8,17 +8,19 @@
 namespace pa {
 
 // Context partitions of a sequence of nblk blocks (nblk >= 1) at pb blocks
-// per partition. Partition p starts at block p * pb and holds pb blocks; the
-// last one runs to the end of the sequence and absorbs a remainder of at
-// most pb / 4 blocks instead of leaving it as a short partition of its own
-// (a short partition's workgroup never fills its load pipeline). Partitions
-// therefore hold up to 5 pb / 4 blocks. Depends only on the length, never on
-// block ids.
+// per partition (pb <= 128). Partition p starts at block p * pb and holds pb
+// blocks; the last one runs to the end of the sequence and absorbs a
+// remainder of at most min(pb / 4, 128 - pb) blocks instead of leaving it as
+// a short partition of its own (a short partition's workgroup never fills
+// its load pipeline). Partitions therefore hold at most 128 blocks, the ids
+// a wave keeps in two registers. Depends only on the length, never on block
+// ids.
 constexpr int kAbsorbDiv = 4;
+constexpr int kMaxPartitionBlocks = 128;
 __host__ __device__ inline int num_parts(int nblk, int pb) {
     const int full = nblk / pb;
     const int rem = nblk - full * pb;
-    const int thr = pb / kAbsorbDiv;
+    const int thr = pb / kAbsorbDiv < kMaxPartitionBlocks - pb ? pb / kAbsorbDiv : kMaxPartitionBlocks - pb;
     const int n = full + (rem > thr ? 1 : 0);
     return n > 1 ? n : 1;
 }

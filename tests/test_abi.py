@@ -76,7 +76,7 @@ def _decode(B, **over):
 
 @pytest.mark.parametrize("over,code", [
     (dict(bs=8), -1), (dict(Hkv=3), -1), (dict(H=0), -1), (dict(nb=0), -1), (dict(mb=0), -1),
-    (dict(mcl=-1), -1), (dict(pb=3), -1), (dict(pb=66), -1), (dict(dt=5), -1), (dict(bits=12), -1),
+    (dict(mcl=-1), -1), (dict(pb=3), -1), (dict(pb=130), -1), (dict(dt=5), -1), (dict(bits=12), -1),
     (dict(d=96), -2), (dict(dt=0, bits=8), -2), (dict(dt=1, bits=32), -2), (dict(H=64, Hkv=2), -2),
     (dict(q=None), -1), (dict(out=None), -1), (dict(tables=None), -1), (dict(bits=8), -1),
     (dict(bits=264), -1), (dict(dt=0, bits=264), -2),
