@@ -139,3 +139,45 @@ def test_other_entry_points_reject_on_host(B):
     bad[19], bad[6], bad[7] = 264, one, one  # fp8 pools: decode only
     assert L.paged_attn_prefill_chunk(*bad) == -2
     assert L.kv_quantize(one, one, one, one, 0, 4, 2, 16, 128, 264, 0, None) == 0   # fp8 accepted
+
+
+def _parts(nblk, pb):
+    """Partitions of nblk blocks at pb per partition, written from the rule the
+    header states: pb each, the last also taking a remainder of up to
+    min(pb / 4, 128 - pb) blocks."""
+    full, rem = divmod(nblk, pb)
+    return max(1, full + (1 if rem > min(pb // 4, 128 - pb) else 0))
+
+
+@pytest.mark.parametrize("S,H,kv,mcl,pb_want", [
+    (64, 32, 8, 3994, 80),      # 2 (sequence, KV head) pairs per CU: at most 80 blocks
+    (64, 32, 8, 16384, 80),
+    (128, 64, 8, 8000, 128),    # many pairs: 128 blocks while 6 workgroups per CU remain
+    (256, 64, 8, 4500, 128),
+    (4, 32, 8, 4096, 8),        # few units: 64 halved down to 4 workgroups per CU
+])
+def test_partition_plan_through_workspace_size(B, S, H, kv, mcl, pb_want):
+    """The library's automatic partition size, read back through the
+    workspace it asks for (a device-free call; 256 compute units assumed
+    without a GPU): 1 MiB of counters plus S * H * pmax rows of d + 2 floats
+    (each part 256-byte aligned), pmax being the partitions of a sequence at
+    max_context_len, plus the prefix pass's slots where it applies."""
+    L = B.lib()
+    d = 128
+    got = L.paged_attn_decode_workspace_size(S, H, kv, d, mcl, 0)
+    forced = L.paged_attn_decode_workspace_size(S, H, kv, d, mcl, pb_want)
+    assert got == forced
+    if S * H // kv < 512:   # no prefix pass: the size is the plain formula
+        pmax = _parts(-(-mcl // 16), pb_want)
+        al = lambda x: (x + 255) // 256 * 256
+        rows = S * H * pmax
+        want = (1 << 20) + al(rows * d * 4) + al(rows * 2 * 4) if pmax > 1 else 0
+        assert got == want
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
