@@ -153,13 +153,13 @@ uint64_t pa_kv_cache_bytes(int n_layers, int n_kv_heads, int d_head, int kv_bits
  *              per-tile runs; it needs no initialisation. One workspace serves
  *              calls of any shape, but calls that share it must be ordered
  *              (same stream, or synchronised): overlapping calls race.
- * partition_blocks  blocks per context partition pb (even, 2..128), or 0 to
+ * partition_blocks  blocks per context partition pb (even, 2..256), or 0 to
  *              let the library choose (from the arguments' values alone). Long contexts are split into
  *              partitions processed in parallel and merged by log-sum-exp
  *              within the same launch: the last partition of a (sequence,
  *              KV head) to finish merges them, in partition order. Partition
  *              p starts at block b0 + p * pb; the last one also takes a
- *              remainder of up to min(pb / 4, 128 - pb) blocks. b0 is 0
+ *              remainder of up to min(pb / 4, 256 - pb) blocks. b0 is 0
  *              unless the prefix pass below took a run of the sequence's
  *              first blocks (then b0 is the run's length). The split depends only on the
  *              arguments' values on the host, each sequence's length and

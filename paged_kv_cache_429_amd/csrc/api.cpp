@@ -50,17 +50,30 @@ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // Blocks per partition. Depends only on host-side shape arguments (never on
 // device data or physical block ids), so a given set of arguments always
 // splits every sequence at the same logical positions. Large partitions
-// (80 to 128 blocks) amortise each workgroup's start and the merge of its
-// partial; they are taken, largest first, while a batch at max_context_len
-// would still give six workgroups per compute unit. With at most two
-// (sequence, KV head) pairs per compute unit, a ragged batch has too few
-// units to balance, and partitions stay at 80 blocks or fewer. Otherwise 64,
-// halved until four workgroups per compute unit.
+// amortise each workgroup's start and the merge of its partial, and a
+// sequence that fits one partition needs no merge at all; but one workgroup
+// streams its partition alone, so with few (sequence, KV head) pairs a
+// ragged batch needs short partitions to balance. Hence, by pairs per
+// compute unit:
+//   more than two: 256 blocks while a batch at max_context_len still gives
+//     four workgroups per compute unit;
+//   at most one: 256 blocks while it still gives one per compute unit;
+//   otherwise (or when those fail): 80 to 128 blocks, largest first, while
+//     it gives six per compute unit (at most 80 with two pairs per unit or
+//     fewer); then 64, halved until four workgroups per compute unit.
+// 256 is taken only when a sequence at max_context_len still splits in two:
+// the shared-prefix paths (groups and the prefix pass) run only on batches
+// whose sequences can be split.
 int plan_partition_blocks(int num_seqs, int n_kv, int max_context_len, int requested) {
     if (requested > 0) return requested;
     const int max_blocks = std::max(1, ceil_div(max_context_len, PA_BLOCK_SIZE));
     const long pairs = (long)num_seqs * n_kv;
     const long cus = cu_count();
+    const int big = pa::kMaxPartitionBlocks;
+    const int big_parts = pa::num_parts(max_blocks, big);
+    const long big_units = pairs * big_parts;
+    if (big_parts > 1 && pairs > 2 * cus && big_units >= 4 * cus) return big;
+    if (big_parts > 1 && pairs <= cus && big_units >= cus) return big;
     const int cap = pairs > 2 * cus ? 128 : 80;
     for (int pb : {128, 112, 96, 80}) {
         if (pb <= cap && pairs * pa::num_parts(max_blocks, pb) >= 6 * cus) return pb;
@@ -139,7 +152,7 @@ uint64_t pa_kv_cache_bytes(int n_layers, int n_kv_heads, int d_head, int kv_bits
 size_t paged_attn_decode_workspace_size(int num_seqs, int n_heads, int n_kv_heads, int d_head,
                                         int max_context_len, int partition_blocks) {
     if (num_seqs <= 0 || n_heads <= 0 || n_kv_heads <= 0 || d_head <= 0 || max_context_len <= 0) return 0;
-    if (partition_blocks < 0 || partition_blocks > 128 || (partition_blocks & 1)) return 0;
+    if (partition_blocks < 0 || partition_blocks > pa::kMaxPartitionBlocks || (partition_blocks & 1)) return 0;
     if (n_heads % n_kv_heads != 0) return 0;
     const int pb = plan_partition_blocks(num_seqs, n_kv_heads, max_context_len, partition_blocks);
     const int pmax = pa::num_parts(ceil_div(max_context_len, PA_BLOCK_SIZE), pb);
@@ -160,7 +173,7 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool, const uin
     if (window < 0) return PA_ERR_INVALID_ARG;
     if (!valid_common(num_seqs, num_blocks, block_size, n_heads, n_kv_heads, d_head)) return PA_ERR_INVALID_ARG;
     if (max_blocks_per_seq <= 0 || max_context_len < 0) return PA_ERR_INVALID_ARG;
-    if (partition_blocks < 0 || partition_blocks > 128 || (partition_blocks & 1)) return PA_ERR_INVALID_ARG;
+    if (partition_blocks < 0 || partition_blocks > pa::kMaxPartitionBlocks || (partition_blocks & 1)) return PA_ERR_INVALID_ARG;
     const int fmt = fmt_of(dtype, kv_bits);
     if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID_ARG;
     if (!valid_kv_bits(kv_bits)) return PA_ERR_INVALID_ARG;

@@ -82,12 +82,10 @@ void decode_kernel(DecodeParams p) {
     // instead of one memory round trip later.
     const int32_t* trow = p.tables + (size_t)u.s * p.max_blocks;
     const bool ids_early = FMT != FMT_F32 && p.prefix_ts == 0 && p.window == 0;
-    int id_lo = 0, id_hi = 0;
+    int wave_ids = 0;
     if (ids_early) {
         const int first = u.part * p.pb;  // < blocks of a sequence at ctx_cap <= max_blocks
-        const int avail = p.max_blocks - first;
-        id_lo = load_ids(trow, first, min(avail, 64), p.num_blocks);
-        id_hi = avail > 64 ? load_ids(trow, first + 64, min(avail - 64, 64), p.num_blocks) : 0;
+        wave_ids = load_wave_ids(trow, first, min(p.max_blocks - first, kMaxPartitionBlocks), p.num_blocks);
     }
     u.ctx = min(p.ctx[u.s], p.ctx_cap);
     if (u.ctx <= 0) {
@@ -137,12 +135,8 @@ void decode_kernel(DecodeParams p) {
         __syncthreads();
         f32_wave<D>(p, u, trow, st, qs);
     } else {
-        if (!ids_early) {
-            const int nbp = u.b_end - u.b_begin;
-            id_lo = load_ids(trow, u.b_begin, min(nbp, 64), p.num_blocks);
-            id_hi = nbp > 64 ? load_ids(trow, u.b_begin + 64, nbp - 64, p.num_blocks) : 0;
-        }
-        mfma_wave<D, FMT>(p, u, id_lo, id_hi, st);
+        if (!ids_early) wave_ids = load_wave_ids(trow, u.b_begin, u.b_end - u.b_begin, p.num_blocks);
+        mfma_wave<D, FMT>(p, u, wave_ids, st);
     }
     epilogue<D, F32OUT>(p, u, st, scratch, kCap);
 }

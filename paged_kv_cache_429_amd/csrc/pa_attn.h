@@ -35,12 +35,27 @@ struct Unit {
     int s, kvh, part, ctx, nblk, nparts, b_begin, b_end, slot0, lo;
 };
 
-// Physical id of block j (wave-uniform, 0 <= j < 128) of a partition whose
-// ids are spread over two lane registers (blocks 0..63 and 64..127).
-__device__ __forceinline__ int tile_id(int id_lo, int id_hi, int j) {
-    const int a = readlane(id_lo, j & 63);
-    const int b = readlane(id_hi, j & 63);
-    return j < 64 ? a : b;
+// Block ids of a partition, spread over its four waves. Wave w visits the
+// pairs w, w + 4, w + 8, ..., so lane 2n + e of its id register holds the id
+// of block 2 (w + 4n) + e of the partition: 64 lanes cover the wave's share
+// of up to 256 blocks. Blocks at or past nb, and ids outside the pool, read
+// as 0 (never dereferenced past the pool).
+__device__ __forceinline__ int load_wave_ids(const int32_t* trow, int first, int nb, int num_blocks) {
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int j = 2 * (w + kWaves * (lane >> 1)) + (lane & 1);
+    int id = 0;
+    if (j < nb) {
+        id = trow[first + j];
+        if ((unsigned)id >= (unsigned)num_blocks) id = 0;
+    }
+    return id;
+}
+
+// Id of block e (0 or 1) of pair k, one of this wave's pairs (k = w + 4n,
+// wave-uniform), from the register load_wave_ids filled.
+__device__ __forceinline__ int pair_id(int ids, int k, int e) {
+    return readlane(ids, 2 * (k / kWaves) + e);
 }
 
 // -----------------------------------------------------------------------------
@@ -664,8 +679,7 @@ __device__ __forceinline__ int pair_run_deep(const DecodeParams& p, int kvh, con
 // wave + 4, ... of the partition, the G query heads of the KV head in
 // columns 0..G-1.
 template <int D, int FMT>
-__device__ __forceinline__ void mfma_wave(const DecodeParams& p, const Unit& u, int id_lo, int id_hi,
-                                          WaveState<D>& st) {
+__device__ __forceinline__ void mfma_wave(const DecodeParams& p, const Unit& u, int wave_ids, WaveState<D>& st) {
     using M = Mfma<D, FMT>;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -681,8 +695,8 @@ __device__ __forceinline__ void mfma_wave(const DecodeParams& p, const Unit& u, 
     if (wave < npairs) {
         // a missing second block repeats the first, which is then masked out
         auto ids = [&](int k, int& i0, int& i1) {
-            i0 = tile_id(id_lo, id_hi, 2 * k);
-            i1 = (2 * k + 1) < nb_part ? tile_id(id_lo, id_hi, 2 * k + 1) : i0;
+            i0 = pair_id(wave_ids, k, 0);
+            i1 = (2 * k + 1) < nb_part ? pair_id(wave_ids, k, 1) : i0;
         };
         auto geo = [&](int k, int& t0, int& ctx, bool& has1) {
             t0 = (u.b_begin + 2 * k) * kBlock;
@@ -1198,12 +1212,11 @@ __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, Wav
     const int col = lane & 15;
     const int q = lane >> 4;
     const int owner = col / G;  // sequence of this column within its column set
-    int my_id[NS], my_hi[NS];
+    int my_id[NS];
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
         const int32_t* trow = p.tables + (size_t)(s0 + i) * p.max_blocks;
-        my_id[i] = load_ids(trow, b, min(nbp[i], 64), p.num_blocks);
-        my_hi[i] = nbp[i] > 64 ? load_ids(trow, b + 64, nbp[i] - 64, p.num_blocks) : 0;
+        my_id[i] = load_wave_ids(trow, b, nbp[i], p.num_blocks);
     }
 
     u32x4 qop[CS][M::KSTEPS];
@@ -1217,14 +1230,14 @@ __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, Wav
     // blocks, full, at the same physical ids.
     auto shared_pair = [&](int k) {
         const int t0 = (b + 2 * k) * kBlock;
-        const int a0 = tile_id(my_id[0], my_hi[0], 2 * k);
-        const int a1 = tile_id(my_id[0], my_hi[0], 2 * k + 1);
+        const int a0 = pair_id(my_id[0], k, 0);
+        const int a1 = pair_id(my_id[0], k, 1);
         bool sh = true;
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
             if (i < NS) {
-                sh = sh && t0 + 2 * kBlock <= ctx[i] && tile_id(my_id[i], my_hi[i], 2 * k) == a0 &&
-                     tile_id(my_id[i], my_hi[i], 2 * k + 1) == a1;
+                sh = sh && t0 + 2 * kBlock <= ctx[i] && pair_id(my_id[i], k, 0) == a0 &&
+                     pair_id(my_id[i], k, 1) == a1;
             }
         }
         return sh;
@@ -1238,8 +1251,8 @@ __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, Wav
         k = pair_run<D, FMT, false>(
             p, kvh, qop[0], cst[0], k,
             [&](int kk, int& i0, int& i1) {
-                i0 = tile_id(my_id[0], my_hi[0], 2 * kk);
-                i1 = tile_id(my_id[0], my_hi[0], 2 * kk + 1);
+                i0 = pair_id(my_id[0], kk, 0);
+                i1 = pair_id(my_id[0], kk, 1);
             },
             [&](int kk) { return kk < npmax && shared_pair(kk); },
             [&](int kk, int& t0, int& cx, bool& has1) {
@@ -1257,8 +1270,8 @@ __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, Wav
                 pair_run<D, FMT, true>(
                     p, kvh, qop[0], cst[0], k,
                     [&](int kk, int& i0, int& i1) {
-                        i0 = tile_id(my_id[i], my_hi[i], 2 * kk);
-                        i1 = (2 * kk + 1) < nbp[i] ? tile_id(my_id[i], my_hi[i], 2 * kk + 1) : i0;
+                        i0 = pair_id(my_id[i], kk, 0);
+                        i1 = (2 * kk + 1) < nbp[i] ? pair_id(my_id[i], kk, 1) : i0;
                     },
                     [&](int kk) { return kk < npairs[i]; },
                     [&](int kk, int& t0, int& cx, bool& has1) {

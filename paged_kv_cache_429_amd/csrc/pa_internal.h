@@ -8,15 +8,15 @@
 namespace pa {
 
 // Context partitions of a sequence of nblk blocks (nblk >= 1) at pb blocks
-// per partition (pb <= 128). Partition p starts at block p * pb and holds pb
+// per partition (pb <= 256). Partition p starts at block p * pb and holds pb
 // blocks; the last one runs to the end of the sequence and absorbs a
-// remainder of at most min(pb / 4, 128 - pb) blocks instead of leaving it as
+// remainder of at most min(pb / 4, 256 - pb) blocks instead of leaving it as
 // a short partition of its own (a short partition's workgroup never fills
-// its load pipeline). Partitions therefore hold at most 128 blocks, the ids
-// a wave keeps in two registers. Depends only on the length, never on block
-// ids.
+// its load pipeline). Partitions therefore hold at most 256 blocks: each of
+// the four waves keeps the ids of its 64 blocks in one register. Depends
+// only on the length, never on block ids.
 constexpr int kAbsorbDiv = 4;
-constexpr int kMaxPartitionBlocks = 128;
+constexpr int kMaxPartitionBlocks = 256;
 __host__ __device__ inline int num_parts(int nblk, int pb) {
     const int full = nblk / pb;
     const int rem = nblk - full * pb;

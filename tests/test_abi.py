@@ -76,7 +76,7 @@ def _decode(B, **over):
 
 @pytest.mark.parametrize("over,code", [
     (dict(bs=8), -1), (dict(Hkv=3), -1), (dict(H=0), -1), (dict(nb=0), -1), (dict(mb=0), -1),
-    (dict(mcl=-1), -1), (dict(pb=3), -1), (dict(pb=130), -1), (dict(dt=5), -1), (dict(bits=12), -1),
+    (dict(mcl=-1), -1), (dict(pb=3), -1), (dict(pb=258), -1), (dict(dt=5), -1), (dict(bits=12), -1),
     (dict(d=96), -2), (dict(dt=0, bits=8), -2), (dict(dt=1, bits=32), -2), (dict(H=64, Hkv=2), -2),
     (dict(q=None), -1), (dict(out=None), -1), (dict(tables=None), -1), (dict(bits=8), -1),
     (dict(bits=264), -1), (dict(dt=0, bits=264), -2),
@@ -144,16 +144,19 @@ def test_other_entry_points_reject_on_host(B):
 def _parts(nblk, pb):
     """Partitions of nblk blocks at pb per partition, written from the rule the
     header states: pb each, the last also taking a remainder of up to
-    min(pb / 4, 128 - pb) blocks."""
+    min(pb / 4, 256 - pb) blocks."""
     full, rem = divmod(nblk, pb)
-    return max(1, full + (1 if rem > min(pb // 4, 128 - pb) else 0))
+    return max(1, full + (1 if rem > min(pb // 4, 256 - pb) else 0))
 
 
 @pytest.mark.parametrize("S,H,kv,mcl,pb_want", [
     (64, 32, 8, 3994, 80),      # 2 (sequence, KV head) pairs per CU: at most 80 blocks
     (64, 32, 8, 16384, 80),
-    (128, 64, 8, 8000, 128),    # many pairs: 128 blocks while 6 workgroups per CU remain
-    (256, 64, 8, 4500, 128),
+    (128, 64, 8, 8000, 256),    # many pairs: 256 blocks while 4 workgroups per CU remain
+    (256, 64, 8, 4500, 256),
+    (256, 32, 8, 4096, 128),    # 256 would leave every sequence whole: 128 while 6 per CU remain
+    (16, 32, 8, 16384, 256),    # at most one pair per CU: 256 while one workgroup per CU remains
+    (32, 32, 8, 4096, 64),      # ... unless sequences stay whole
     (4, 32, 8, 4096, 8),        # few units: 64 halved down to 4 workgroups per CU
 ])
 def test_partition_plan_through_workspace_size(B, S, H, kv, mcl, pb_want):

@@ -53,18 +53,18 @@ def test_shapes(lib, n_heads, n_kv, d, dtype):
     _parity(c)
 
 
-@pytest.mark.parametrize("pb", [2, 4, 8, 16, 32, 64, 80, 96, 112, 128])
+@pytest.mark.parametrize("pb", [2, 4, 8, 16, 32, 64, 80, 96, 112, 128, 160, 192, 256])
 def test_partition_invariance(lib, pb):
     c = make_config_case(2, num_seqs=12)
     _parity(c, partition_blocks=pb)
 
 
-@pytest.mark.parametrize("pb", [2, 16, 64, 96, 128])
+@pytest.mark.parametrize("pb", [2, 16, 64, 96, 128, 208, 256])
 def test_partition_rounding_boundaries(lib, pb):
     """Partitions hold pb blocks, the last one absorbing a remainder of up
-    to min(pb / 4, 128 - pb) blocks (so beyond 64 blocks at pb = 64, never
-    beyond 128): lengths around every boundary of that rule."""
-    r = max(1, min(pb // 4, 128 - pb))
+    to min(pb / 4, 256 - pb) blocks (so beyond 64 blocks at pb = 64, never
+    beyond 256): lengths around every boundary of that rule."""
+    r = max(1, min(pb // 4, 256 - pb))
     nb = [pb - 1, pb, pb + 1, pb + r - 1, pb + r, pb + r + 1, 2 * pb, 2 * pb + r, 2 * pb + r + 1, 3 * pb - 1]
     ctx = sorted({max(1, 16 * n - 3) for n in nb} | {max(1, 16 * n) for n in nb})
     c = make_decode_case(16, 4, 128, "bf16", ctx, 330 + pb, pool_factor=1.2)
