@@ -184,7 +184,7 @@ uint64_t pa_kv_cache_bytes(int n_layers, int n_kv_heads, int d_head, int kv_bits
  *                processed together, by the workgroup of the group's first
  *                sequence, each shared block being read once for the group;
  *                results are bit-identical to those of private copies of
- *                the same blocks.
+ *                the same blocks. With bf16 pools, only when pb <= 128.
  * ------------------------------------------------------------------------ */
 size_t paged_attn_decode_workspace_size(int num_seqs, int n_heads, int n_kv_heads, int d_head,
                                         int max_context_len, int partition_blocks);

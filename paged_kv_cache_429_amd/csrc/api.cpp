@@ -213,7 +213,10 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool, const uin
     // group's first sequence) for the MFMA formats at G = 4 or 8, when
     // sequences can be split and the batch holds a whole group.
     p.share_n = 0;
-    if (fmt != 0 && p.pmax > 1 && window == 0 && (G == 4 || G == 8) && num_seqs >= 16 / G) p.share_n = 16 / G;
+    // (bf16 keeps the group's ids for at most 128 blocks per partition).
+    if (fmt != 0 && p.pmax > 1 && window == 0 && (G == 4 || G == 8) && num_seqs >= 16 / G &&
+        (fmt != 1 || p.pb <= 128))
+        p.share_n = 16 / G;
     // Prefix pass (bf16 pools): a launch before the decode that attends each
     // tile's common leading run of blocks for all its rows at once.
     p.kpmax = fmt == 1 && window == 0 ? plan_prefix_parts(num_seqs, n_heads, n_kv_heads, d_head, p.ctx_cap, p.pmax)

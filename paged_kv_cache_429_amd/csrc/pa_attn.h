@@ -1177,6 +1177,35 @@ __device__ __forceinline__ bool group_shares(const DecodeParams& p, int s0, int 
     return ok;
 }
 
+// Block ids of a partition as the shared-group path holds them, one set per
+// sequence of the group. bf16 keeps the partition's blocks 0-63 and 64-127
+// in two lane registers (partitions of at most 128 blocks): with one
+// register per wave its group path no longer fits the register budget of
+// three waves per SIMD and spills. The other formats run at two waves per
+// SIMD and keep the per-wave layout of the per-sequence path (up to 256).
+struct SpanIds {
+    int lo, hi;
+    __device__ __forceinline__ void load(const int32_t* trow, int first, int nb, int num_blocks) {
+        lo = load_ids(trow, first, min(nb, 64), num_blocks);
+        hi = nb > 64 ? load_ids(trow, first + 64, nb - 64, num_blocks) : 0;
+    }
+    // id of block e of pair k (wave-uniform k, 2k + e < 128)
+    __device__ __forceinline__ int get(int k, int e) const {
+        const int j = 2 * k + e;
+        const int a = readlane(lo, j & 63);
+        const int b = readlane(hi, j & 63);
+        return j < 64 ? a : b;
+    }
+};
+
+struct WaveIds {
+    int r;
+    __device__ __forceinline__ void load(const int32_t* trow, int first, int nb, int num_blocks) {
+        r = load_wave_ids(trow, first, nb, num_blocks);
+    }
+    __device__ __forceinline__ int get(int k, int e) const { return pair_id(r, k, e); }
+};
+
 template <int D, int FMT, int CS, int NS, bool F32OUT>
 __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, WaveState<D>& st, float* merge_scratch,
                                             int cap) {
@@ -1212,11 +1241,12 @@ __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, Wav
     const int col = lane & 15;
     const int q = lane >> 4;
     const int owner = col / G;  // sequence of this column within its column set
-    int my_id[NS];
+    using Ids = std::conditional_t<FMT == FMT_BF16, SpanIds, WaveIds>;
+    Ids my_id[NS];
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
         const int32_t* trow = p.tables + (size_t)(s0 + i) * p.max_blocks;
-        my_id[i] = load_wave_ids(trow, b, nbp[i], p.num_blocks);
+        my_id[i].load(trow, b, nbp[i], p.num_blocks);
     }
 
     u32x4 qop[CS][M::KSTEPS];
@@ -1230,14 +1260,13 @@ __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, Wav
     // blocks, full, at the same physical ids.
     auto shared_pair = [&](int k) {
         const int t0 = (b + 2 * k) * kBlock;
-        const int a0 = pair_id(my_id[0], k, 0);
-        const int a1 = pair_id(my_id[0], k, 1);
+        const int a0 = my_id[0].get(k, 0);
+        const int a1 = my_id[0].get(k, 1);
         bool sh = true;
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
             if (i < NS) {
-                sh = sh && t0 + 2 * kBlock <= ctx[i] && pair_id(my_id[i], k, 0) == a0 &&
-                     pair_id(my_id[i], k, 1) == a1;
+                sh = sh && t0 + 2 * kBlock <= ctx[i] && my_id[i].get(k, 0) == a0 && my_id[i].get(k, 1) == a1;
             }
         }
         return sh;
@@ -1251,8 +1280,8 @@ __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, Wav
         k = pair_run<D, FMT, false>(
             p, kvh, qop[0], cst[0], k,
             [&](int kk, int& i0, int& i1) {
-                i0 = pair_id(my_id[0], kk, 0);
-                i1 = pair_id(my_id[0], kk, 1);
+                i0 = my_id[0].get(kk, 0);
+                i1 = my_id[0].get(kk, 1);
             },
             [&](int kk) { return kk < npmax && shared_pair(kk); },
             [&](int kk, int& t0, int& cx, bool& has1) {
@@ -1270,8 +1299,8 @@ __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, Wav
                 pair_run<D, FMT, true>(
                     p, kvh, qop[0], cst[0], k,
                     [&](int kk, int& i0, int& i1) {
-                        i0 = pair_id(my_id[i], kk, 0);
-                        i1 = (2 * kk + 1) < nbp[i] ? pair_id(my_id[i], kk, 1) : i0;
+                        i0 = my_id[i].get(kk, 0);
+                        i1 = (2 * kk + 1) < nbp[i] ? my_id[i].get(kk, 1) : i0;
                     },
                     [&](int kk) { return kk < npairs[i]; },
                     [&](int kk, int& t0, int& cx, bool& has1) {
