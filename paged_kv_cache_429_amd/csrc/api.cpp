@@ -61,10 +61,14 @@ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 //   otherwise (or when those fail): 80 to 128 blocks, largest first, while
 //     it gives six per compute unit (at most 80 with two pairs per unit or
 //     fewer); then 64, halved until four workgroups per compute unit.
-// 256 is taken only when a sequence at max_context_len still splits in two:
-// the shared-prefix paths (groups and the prefix pass) run only on batches
-// whose sequences can be split.
-int plan_partition_blocks(int num_seqs, int n_kv, int max_context_len, int requested) {
+// On shapes the prefix pass applies to, 256 is taken only when a sequence at
+// max_context_len still splits in two: unsplit, a batch that shares nothing
+// still pays for the pass, and its cost is no longer hidden by a merge the
+// split needs anyway (128 x U[512,4096], 32/8/128: 202 us unsplit against
+// 197 us at 128 blocks).
+int plan_prefix_parts(int num_seqs, int n_heads, int n_kv, int d, int ctx_cap);
+
+int plan_partition_blocks(int num_seqs, int n_heads, int n_kv, int d, int max_context_len, int requested) {
     if (requested > 0) return requested;
     const int max_blocks = std::max(1, ceil_div(max_context_len, PA_BLOCK_SIZE));
     const long pairs = (long)num_seqs * n_kv;
@@ -72,8 +76,9 @@ int plan_partition_blocks(int num_seqs, int n_kv, int max_context_len, int reque
     const int big = pa::kMaxPartitionBlocks;
     const int big_parts = pa::num_parts(max_blocks, big);
     const long big_units = pairs * big_parts;
-    if (big_parts > 1 && pairs > 2 * cus && big_units >= 4 * cus) return big;
-    if (big_parts > 1 && pairs <= cus && big_units >= cus) return big;
+    const bool big_ok = big_parts > 1 || plan_prefix_parts(num_seqs, n_heads, n_kv, d, max_context_len) == 0;
+    if (big_ok && pairs > 2 * cus && big_units >= 4 * cus) return big;
+    if (big_ok && pairs <= cus && big_units >= cus) return big;
     const int cap = pairs > 2 * cus ? 128 : 80;
     for (int pb : {128, 112, 96, 80}) {
         if (pb <= cap && pairs * pa::num_parts(max_blocks, pb) >= 6 * cus) return pb;
@@ -95,9 +100,9 @@ int plan_partition_blocks(int num_seqs, int n_kv, int max_context_len, int reque
 // the run is split so that the pass has about one workgroup per compute
 // unit, each range holding at least kMinPrefixBlocks blocks. The element
 // format is checked by the caller (bf16 pools only).
-int plan_prefix_parts(int num_seqs, int n_heads, int n_kv, int d, int ctx_cap, int pmax) {
+int plan_prefix_parts(int num_seqs, int n_heads, int n_kv, int d, int ctx_cap) {
     const int G = n_heads / n_kv;
-    if (d != 128 || G <= 0 || 32 % G != 0 || pmax <= 1) return 0;
+    if (d != 128 || G <= 0 || 32 % G != 0) return 0;
     if ((long)num_seqs * G < 2L * pa::kPrefixRows) return 0;
     const int max_run = (ctx_cap - 1) / PA_BLOCK_SIZE;
     if (max_run < pa::kMinPrefixBlocks) return 0;
@@ -154,9 +159,9 @@ size_t paged_attn_decode_workspace_size(int num_seqs, int n_heads, int n_kv_head
     if (num_seqs <= 0 || n_heads <= 0 || n_kv_heads <= 0 || d_head <= 0 || max_context_len <= 0) return 0;
     if (partition_blocks < 0 || partition_blocks > pa::kMaxPartitionBlocks || (partition_blocks & 1)) return 0;
     if (n_heads % n_kv_heads != 0) return 0;
-    const int pb = plan_partition_blocks(num_seqs, n_kv_heads, max_context_len, partition_blocks);
+    const int pb = plan_partition_blocks(num_seqs, n_heads, n_kv_heads, d_head, max_context_len, partition_blocks);
     const int pmax = pa::num_parts(ceil_div(max_context_len, PA_BLOCK_SIZE), pb);
-    const int kpmax = plan_prefix_parts(num_seqs, n_heads, n_kv_heads, d_head, max_context_len, pmax);
+    const int kpmax = plan_prefix_parts(num_seqs, n_heads, n_kv_heads, d_head, max_context_len);
     return pa::decode_workspace_bytes(num_seqs, n_heads, n_kv_heads, d_head, pmax, kpmax);
 }
 
@@ -203,23 +208,22 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool, const uin
     p.n_kv = n_kv_heads;
     p.group = G;
     // planned from max_context_len exactly as paged_attn_decode_workspace_size() does
-    p.pb = plan_partition_blocks(num_seqs, n_kv_heads, std::max(1, max_context_len), partition_blocks);
+    p.pb = plan_partition_blocks(num_seqs, n_heads, n_kv_heads, d_head, std::max(1, max_context_len), partition_blocks);
     p.pmax = pa::num_parts(ceil_div(std::max(1, p.ctx_cap), PA_BLOCK_SIZE), p.pb);
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d_head));
     p.window = window;
 
     // Shared-prefix groups (16/G consecutive sequences whose tables name the
     // same blocks fill the 16 MFMA columns, computed by the workgroup of the
-    // group's first sequence) for the MFMA formats at G = 4 or 8, when
-    // sequences can be split and the batch holds a whole group.
+    // group's first sequence) for the MFMA formats at G = 4 or 8, when the
+    // batch holds a whole group.
     p.share_n = 0;
     // (bf16 keeps the group's ids for at most 128 blocks per partition).
-    if (fmt != 0 && p.pmax > 1 && window == 0 && (G == 4 || G == 8) && num_seqs >= 16 / G &&
-        (fmt != 1 || p.pb <= 128))
+    if (fmt != 0 && window == 0 && (G == 4 || G == 8) && num_seqs >= 16 / G && (fmt != 1 || p.pb <= 128))
         p.share_n = 16 / G;
     // Prefix pass (bf16 pools): a launch before the decode that attends each
     // tile's common leading run of blocks for all its rows at once.
-    p.kpmax = fmt == 1 && window == 0 ? plan_prefix_parts(num_seqs, n_heads, n_kv_heads, d_head, p.ctx_cap, p.pmax)
+    p.kpmax = fmt == 1 && window == 0 ? plan_prefix_parts(num_seqs, n_heads, n_kv_heads, d_head, p.ctx_cap)
                                       : 0;
     p.pslots = p.pmax + p.kpmax;
     p.prefix_ts = p.kpmax > 0 ? pa::kPrefixRows / G : 0;

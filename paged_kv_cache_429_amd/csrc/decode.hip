@@ -151,7 +151,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // one plan entry per tile (num_seqs entries bound the tile count).
 size_t decode_workspace_bytes(int num_seqs, int n_heads, int n_kv, int d, int pmax, int kpmax) {
     (void)n_kv;
-    if (pmax <= 1) return 0;
+    if (pmax <= 1 && kpmax == 0) return 0;  // nothing is split: no partials
     const size_t rows = (size_t)num_seqs * n_heads * (pmax + kpmax);
     const size_t plan = kpmax > 0 ? align256((size_t)num_seqs * sizeof(int)) : 0;
     return kCounterBytes + align256(rows * d * sizeof(float)) + align256(rows * 2 * sizeof(float)) + plan;

@@ -154,9 +154,12 @@ def _parts(nblk, pb):
     (64, 32, 8, 16384, 80),
     (128, 64, 8, 8000, 256),    # many pairs: 256 blocks while 4 workgroups per CU remain
     (256, 64, 8, 4500, 256),
-    (256, 32, 8, 4096, 128),    # 256 would leave every sequence whole: 128 while 6 per CU remain
+    (256, 32, 8, 4096, 128),    # whole sequences at 256, on a shape the prefix pass takes: 128
+    (256, 48, 16, 4096, 256),   # G = 3 (no 32-row MFMA tile): no prefix pass, every sequence whole
+    (128, 16, 8, 4096, 256),    # G = 2, 256 query rows per KV head: no prefix pass, whole
     (16, 32, 8, 16384, 256),    # at most one pair per CU: 256 while one workgroup per CU remains
-    (32, 32, 8, 4096, 64),      # ... unless sequences stay whole
+    (32, 32, 8, 4096, 256),
+    (16, 32, 8, 4096, 32),      # too few workgroups at 256: 64 halved down to 4 per CU
     (4, 32, 8, 4096, 8),        # few units: 64 halved down to 4 workgroups per CU
 ])
 def test_partition_plan_through_workspace_size(B, S, H, kv, mcl, pb_want):
@@ -176,6 +179,17 @@ def test_partition_plan_through_workspace_size(B, S, H, kv, mcl, pb_want):
         rows = S * H * pmax
         want = (1 << 20) + al(rows * d * 4) + al(rows * 2 * 4) if pmax > 1 else 0
         assert got == want
+
+
+def test_workspace_when_no_sequence_splits(B):
+    """One partition per sequence needs no workspace, unless the prefix pass
+    applies (d 128, G dividing 32, at least 512 query rows per KV head): its
+    partials and per-tile runs still need one."""
+    L = B.lib()
+    assert L.paged_attn_decode_workspace_size(128, 16, 8, 128, 4096, 256) == 0      # G = 2, 256 rows
+    assert L.paged_attn_decode_workspace_size(256, 48, 16, 128, 4096, 256) == 0     # G = 3
+    assert L.paged_attn_decode_workspace_size(256, 32, 8, 128, 4096, 256) > (1 << 20)  # G = 4, 1024 rows
+    assert L.paged_attn_decode_workspace_size(256, 32, 8, 64, 4096, 256) == 0       # d 64: no pass
 
 
 def test_bench_refuses_more_than_one_gpu():

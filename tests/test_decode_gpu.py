@@ -111,7 +111,7 @@ CLUSTERS = [
 
 
 @pytest.mark.parametrize("n_heads,n_kv", [(32, 4), (16, 4), (64, 8)])
-@pytest.mark.parametrize("pb", [0, 2, 4, 16, 64])
+@pytest.mark.parametrize("pb", [0, 2, 4, 16, 64, 128])  # 128: no sequence split
 def test_shared_prefix_clusters_bitexact(lib, n_heads, n_kv, pb):
     """Shared blocks give bit-identical output to private copies of the same
     data, whichever path computes each partition, and match the oracle."""
@@ -132,8 +132,9 @@ def _quantize_ref(slots, bits):
     return oracle.dequantize(*oracle.quantize_tiles(x, bits))
 
 
+@pytest.mark.parametrize("pb", [4, 256])  # 256: no sequence split
 @pytest.mark.parametrize("bits", [8, 4, 264])  # 264: fp8 (e4m3)
-def test_shared_prefix_quantized_bitexact(lib, bits):
+def test_shared_prefix_quantized_bitexact(lib, bits, pb):
     from paged_kv_cache_429_amd import binding as B
     outs = []
     c = make_clustered_prefix_case(32, 4, 128, "bf16", CLUSTERS, 320 + bits % 256)
@@ -141,10 +142,10 @@ def test_shared_prefix_quantized_bitexact(lib, bits):
         kp, vp = upload_pools(case)
         kc, ks = B.quantize(kp, bits=bits, kind=0, n_kv_heads=4, d_head=128)
         vc, vs = B.quantize(vp, bits=bits, kind=1, n_kv_heads=4, d_head=128)
-        outs.append(gpu_decode(case, kp=kc, vp=vc, kv_bits=bits, k_scales=ks, v_scales=vs, partition_blocks=4).cpu())
+        outs.append(gpu_decode(case, kp=kc, vp=vc, kv_bits=bits, k_scales=ks, v_scales=vs, partition_blocks=pb).cpu())
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
     ref = oracle_decode(c, k_slots=_quantize_ref(c.k_slots, bits), v_slots=_quantize_ref(c.v_slots, bits))
-    assert_close(dev_to_f64(outs[0]), ref, "bf16", f"clusters kv_bits {bits}")
+    assert_close(dev_to_f64(outs[0]), ref, "bf16", f"clusters kv_bits {bits} pb {pb}")
 
 
 # Long shared prefixes under partitions of more than 128 blocks: a cluster
@@ -208,6 +209,7 @@ def _prefix_tiles(G):
 
 @pytest.mark.parametrize("n_heads,n_kv,pb", [
     (64, 8, 0), (64, 8, 2), (64, 8, 16), (32, 8, 0), (64, 4, 0), (64, 4, 64), (16, 8, 0),
+    (64, 8, 256), (64, 4, 128), (32, 8, 256),   # one partition per sequence: the pass's partials alone
 ])
 def test_prefix_pass_tiles(lib, n_heads, n_kv, pb):
     G = n_heads // n_kv
