@@ -15,9 +15,11 @@
  *   - forked sequences share blocks (reference counts); writing into a shared,
  *     partly filled last block first moves the writer to a fresh copy
  *     (copy-on-write: the caller copies the block's K/V, see pa_copy_blocks);
- *   - a prefix cache: every full block of a prompt is entered under a 64-bit
- *     FNV-1a chain hash of the prompt's tokens up to the block's end; a later
- *     prompt reuses the blocks of its longest cached prefix of whole blocks;
+ *   - a prefix cache: every full block of a prompt is entered under the
+ *     prompt's exact tokens up to the block's end (a trie of 16-token
+ *     blocks, compared token by token, so different prefixes never share an
+ *     entry); a later prompt reuses the blocks of its longest cached prefix
+ *     of whole blocks;
  *   - a scheduler step that admits waiting requests while their prompts fit
  *     in free blocks and preempts the newest running sequence when another
  *     cannot get a block.

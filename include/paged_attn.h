@@ -41,9 +41,10 @@
  * block_tables[s * max_blocks_per_seq + t / 16]. Physical blocks may be
  * shared between sequences (common prefixes, [JE] "Prefix caching"); the
  * kernels follow the table and never write the pool. Only the entries
- * j < ceil(ctx_s / 16) of a row are read. Block ids outside [0, num_blocks)
+ * j < ceil(ctx_s / 16) of a row are used. Block ids outside [0, num_blocks)
  * are a caller error: the kernels replace them by block 0 (never reading out
- * of bounds), so results for that sequence are then meaningless.
+ * of bounds), so results for that sequence are then meaningless, and record
+ * the first such entry; pa_take_block_id_error() reports it.
  *
  * GQA ([IR] "What it is" and the table in "The memory equation"): query head
  * h reads KV head h / G, G = n_heads / n_kv_heads (contiguous groups);
@@ -106,7 +107,7 @@ typedef enum pa_kv_kind { PA_KIND_K = 0, PA_KIND_V = 1 } pa_kv_kind;
 #define PA_MAX_GROUP 16
 /* kv_bits code of OCP fp8 e4m3 pools (8 bits of storage per element). */
 #define PA_KV_FP8 264
-#define PA_DECODE_COUNTER_BYTES (1u << 20)
+#define PA_DECODE_COUNTER_BYTES (2u << 20)
 
 /* Human-readable text of a status code (static storage). */
 const char* pa_error_string(int status);
@@ -142,17 +143,22 @@ uint64_t pa_kv_cache_bytes(int n_layers, int n_kv_heads, int d_head, int kv_bits
  * max_context_len  host-side upper bound of context_lens (plans the split)
  * out          [num_seqs][n_heads][d_head] of dtype (written)
  * workspace    device scratch of at least paged_attn_decode_workspace_size()
- *              bytes (may be NULL when that size is 0). Its first
- *              PA_DECODE_COUNTER_BYTES hold arrival counters, one int32 per
- *              (sequence, KV head), so num_seqs * n_kv_heads may not exceed
- *              PA_DECODE_COUNTER_BYTES / 4 (else PA_ERR_UNSUPPORTED). The
- *              counters must be zero before the first call that uses the
- *              workspace (allocate it zero-filled); every call that completes
- *              leaves them zero again. The rest holds the partials of split
- *              sequences and of the prefix pass, and the prefix pass's
- *              per-tile runs; it needs no initialisation. One workspace serves
- *              calls of any shape, but calls that share it must be ordered
- *              (same stream, or synchronised): overlapping calls race.
+ *              bytes (may be NULL when that size is 0). It needs no
+ *              initialisation. Its first PA_DECODE_COUNTER_BYTES hold
+ *              arrival words, one 64-bit word per (sequence, KV head), so
+ *              num_seqs * n_kv_heads may not exceed
+ *              PA_DECODE_COUNTER_BYTES / 8 (else PA_ERR_UNSUPPORTED). Each
+ *              call tags the words it counts in with an epoch of its own (a
+ *              process-wide 32-bit counter), and a word of any other epoch
+ *              counts as zero arrivals, so neither garbage nor the leftovers
+ *              of a call whose launch died midway affect later calls. (A
+ *              captured launch replays its epoch; it stays correct because
+ *              each completed merge leaves its word at a count of zero.) The
+ *              rest holds the partials of split sequences and of the prefix
+ *              pass, and the prefix pass's per-tile runs. One workspace
+ *              serves calls of any shape, but calls that share it must be
+ *              ordered (same stream, or synchronised): overlapping calls
+ *              race.
  * partition_blocks  blocks per context partition pb (even, 2..256), or 0 to
  *              let the library choose (from the arguments' values alone). Long contexts are split into
  *              partitions processed in parallel and merged by log-sum-exp
@@ -184,7 +190,8 @@ uint64_t pa_kv_cache_bytes(int n_layers, int n_kv_heads, int d_head, int kv_bits
  *                processed together, by the workgroup of the group's first
  *                sequence, each shared block being read once for the group;
  *                results are bit-identical to those of private copies of
- *                the same blocks. With bf16 pools, only when pb <= 128.
+ *                the same blocks. With bf16 pools, only when no partition
+ *                can exceed 128 blocks: pb + min(pb / 4, 256 - pb) <= 128.
  * ------------------------------------------------------------------------ */
 size_t paged_attn_decode_workspace_size(int num_seqs, int n_heads, int n_kv_heads, int d_head,
                                         int max_context_len, int partition_blocks);
@@ -312,6 +319,22 @@ int pa_copy_blocks(void* k_pool, void* v_pool, uint16_t* k_scales, uint16_t* v_s
  * 16-byte loads and writes the XOR of every 32-bit word it read to
  * xor_out[w] (device uint32 [grid]). Nothing else is written.
  * ------------------------------------------------------------------------ */
+/* ---------------------------------------------------------------------------
+ * Block-table check ([IR] "PagedAttention: why fragmentation was eating most
+ * of the rest": the table maps each logical block to a physical block of the
+ * pool). Every kernel that follows a block table checks each entry it uses
+ * against [0, num_blocks); an entry outside it is read as block 0 and the
+ * first such entry per device is recorded (the check costs nothing while
+ * every entry is valid). This takes the record of the current device:
+ * returns 1 and sets *table_index (the entry's index in the block_tables
+ * array of the call that met it: sequence * max_blocks_per_seq + logical
+ * block) and *block_id (either pointer may be NULL), then clears it; returns
+ * 0 if nothing was recorded since the last take; PA_ERR_HIP if the device
+ * could not be read. Host; synchronous. Call it once the kernels of interest
+ * have completed and while no call of this library runs on the device.
+ * ------------------------------------------------------------------------ */
+int pa_take_block_id_error(int64_t* table_index, int32_t* block_id);
+
 int pa_hbm_read_probe(const void* buf, int64_t buf_bytes, int tile_bytes, const int32_t* order, int64_t n_order,
                       uint32_t* xor_out, int grid, void* stream);
 

@@ -25,7 +25,7 @@ BLOCK_SIZE = 16
 EXPORTS = (
     "pa_error_string", "pa_tile_bytes", "pa_kv_bytes_per_token", "pa_kv_cache_bytes",
     "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_decode_window", "paged_attn_prefill_chunk",
-    "kv_quantize", "paged_kv_write", "pa_copy_blocks", "pa_hbm_read_probe",
+    "kv_quantize", "paged_kv_write", "pa_copy_blocks", "pa_hbm_read_probe", "pa_take_block_id_error",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_ref_count", "pa_bm_add", "pa_bm_append",
     "pa_bm_fork", "pa_bm_release", "pa_bm_num_tokens", "pa_bm_table",
     "pa_sched_create", "pa_sched_destroy", "pa_sched_submit", "pa_sched_num_live", "pa_sched_step",
@@ -68,6 +68,8 @@ def _declare(lib):
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.pa_hbm_read_probe.restype = i
     lib.pa_hbm_read_probe.argtypes = [vp, i64, i, vp, i64, vp, i, vp]
+    lib.pa_take_block_id_error.restype = i
+    lib.pa_take_block_id_error.argtypes = [ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_int32)]
     # host block manager and scheduler (opaque handles)
     lib.pa_bm_create.restype = vp
     lib.pa_bm_create.argtypes = [i, i]
@@ -195,8 +197,10 @@ _ws = {}
 def decode_workspace(num_seqs, n_heads, n_kv_heads, d_head, max_context_len, partition_blocks=0,
                      device=None, stream=None):
     """A workspace large enough for the call, cached per (device, stream).
-    It is allocated zero-filled: its leading arrival counters must start at
-    zero, and every completed call leaves them zero."""
+    It needs no initialisation (its arrival words are tagged with each
+    call's epoch). It is allocated from the pool of the stream that uses it,
+    so a buffer it replaces is reused only by work ordered after the calls
+    on that stream."""
     n = int(lib().paged_attn_decode_workspace_size(num_seqs, n_heads, n_kv_heads, d_head, max_context_len,
                                                    partition_blocks))
     if n == 0:
@@ -206,7 +210,8 @@ def decode_workspace(num_seqs, n_heads, n_kv_heads, d_head, max_context_len, par
     key = (device.index, s.cuda_stream)
     buf = _ws.get(key)
     if buf is None or buf.numel() < n:
-        buf = torch.zeros(max(n, 2 << 20), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(s):
+            buf = torch.empty(max(n, 4 << 20), dtype=torch.uint8, device=device)
         _ws[key] = buf
     return buf
 
@@ -299,6 +304,15 @@ def copy_blocks(pairs, k_pool, v_pool, *, n_kv_heads, d_head, kv_bits, k_scales=
     st = lib().pa_copy_blocks(_p(k_pool), _p(v_pool), _p(k_scales), _p(v_scales), _p(pairs), int(pairs.shape[0]),
                               nb, n_kv_heads, d_head, kv_bits, _stream(stream, dev))
     _check("pa_copy_blocks", st)
+
+
+def take_block_id_error():
+    """pa_take_block_id_error: None, or (table index, block id) of the first
+    out-of-range block-table entry a kernel met since the last take."""
+    idx, bid = ctypes.c_int64(-1), ctypes.c_int32(0)
+    r = lib().pa_take_block_id_error(ctypes.byref(idx), ctypes.byref(bid))
+    _check("pa_take_block_id_error", min(r, 0))
+    return (idx.value, bid.value) if r == 1 else None
 
 
 def hbm_read_probe(buf, tile_bytes, *, order=None, grid=2048, xor_out=None, stream=None):

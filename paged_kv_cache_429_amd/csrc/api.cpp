@@ -14,6 +14,7 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];
+std::atomic<unsigned> g_epoch{0};
 
 // Compute units of the current device (cached per device; 256 on MI355X).
 int cu_count() {
@@ -121,6 +122,14 @@ bool valid_common(int num_seqs, int num_blocks, int block_size, int n_heads, int
 
 }  // namespace
 
+namespace pa {
+unsigned next_epoch() {
+    unsigned e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+    if (e == 0) e = g_epoch.fetch_add(1, std::memory_order_relaxed) + 1;
+    return e;
+}
+}  // namespace pa
+
 extern "C" {
 
 const char* pa_error_string(int status) {
@@ -218,8 +227,11 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool, const uin
     // group's first sequence) for the MFMA formats at G = 4 or 8, when the
     // batch holds a whole group.
     p.share_n = 0;
-    // (bf16 keeps the group's ids for at most 128 blocks per partition).
-    if (fmt != 0 && window == 0 && (G == 4 || G == 8) && num_seqs >= 16 / G && (fmt != 1 || p.pb <= 128))
+    // (bf16 keeps the group's ids for at most 128 blocks per partition, so it
+    // takes groups only when no partition, an absorbed remainder included,
+    // can exceed 128 blocks).
+    if (fmt != 0 && window == 0 && (G == 4 || G == 8) && num_seqs >= 16 / G &&
+        (fmt != 1 || pa::max_partition_blocks(p.pb) <= 128))
         p.share_n = 16 / G;
     // Prefix pass (bf16 pools): a launch before the decode that attends each
     // tile's common leading run of blocks for all its rows at once.
@@ -236,6 +248,7 @@ int decode_impl(const void* q, const void* k_pool, const void* v_pool, const uin
                                    &p.part_ml, &p.counters, &plan);
     }
     p.plan = plan;
+    p.epoch = pa::next_epoch();
     const hipStream_t st = static_cast<hipStream_t>(stream);
     if (p.kpmax > 0) {
         pa::PrefillParams pp{};
@@ -368,6 +381,20 @@ int pa_copy_blocks(void* k_pool, void* v_pool, uint16_t* k_scales, uint16_t* v_s
     const hipError_t e = pa::launch_copy_blocks(k_pool, v_pool, k_scales, v_scales, pairs, n_pairs, num_blocks,
                                                 n_kv_heads, block_bytes, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int pa_take_block_id_error(int64_t* table_index, int32_t* block_id) {
+    pa::BadIdRecord r[3] = {};
+    if (pa::take_bad_id_decode(&r[0]) != hipSuccess || pa::take_bad_id_prefill(&r[1]) != hipSuccess ||
+        pa::take_bad_id_kvops(&r[2]) != hipSuccess)
+        return PA_ERR_HIP;
+    for (const auto& x : r) {
+        if (!x.flag) continue;
+        if (table_index) *table_index = ((int64_t)x.idx_hi << 32) | (int64_t)x.idx_lo;
+        if (block_id) *block_id = x.id;
+        return 1;
+    }
+    return 0;
 }
 
 int pa_hbm_read_probe(const void* buf, int64_t buf_bytes, int tile_bytes, const int32_t* order, int64_t n_order,

@@ -10,31 +10,36 @@
 #include "../../include/pa_block_manager.h"
 
 #include <algorithm>
+#include <array>
 #include <cstdint>
 #include <deque>
+#include <map>
 #include <new>
+#include <set>
 #include <unordered_map>
 #include <vector>
 
 namespace {
 
 constexpr int kBlock = PA_BLOCK_SIZE;
+using BlockToks = std::array<int64_t, kBlock>;
 
-// 64-bit FNV-1a (Fowler, Noll, Vo) over the little-endian bytes of `v`.
-uint64_t fnv1a(uint64_t h, uint64_t v) {
-    for (int i = 0; i < 8; ++i) {
-        h ^= (v >> (8 * i)) & 0xffu;
-        h *= 0x100000001b3ull;
-    }
-    return h;
-}
+// Prefix cache as a trie over whole blocks: the node reached from the root
+// by the token contents of blocks 0..i of a prompt stands for that exact
+// prefix, and holds the physical block cached for its last block (-1 when
+// none is). Lookups compare token contents exactly, so two different
+// prefixes never share an entry.
+struct Node {
+    Node* parent = nullptr;
+    BlockToks toks{};
+    std::map<BlockToks, Node*> kids;
+    int32_t block = -1;
+};
 
-// Chain hash of a full block: the previous block's hash (0 for the first)
-// then its 16 tokens, hashed from the FNV offset basis.
-uint64_t chain_hash(uint64_t parent, const int64_t* toks) {
-    uint64_t h = fnv1a(0xcbf29ce484222325ull, parent);
-    for (int i = 0; i < kBlock; ++i) h = fnv1a(h, (uint64_t)toks[i]);
-    return h;
+BlockToks block_toks(const int64_t* t) {
+    BlockToks b;
+    std::copy(t, t + kBlock, b.begin());
+    return b;
 }
 
 struct Seq {
@@ -55,10 +60,19 @@ struct pa_block_manager {
     int32_t head = -1, tail = -1;
     int n_evictable = 0;
     std::vector<int32_t> ref;
-    std::vector<uint8_t> cached;
-    std::vector<uint64_t> key_of;
-    std::unordered_map<uint64_t, int32_t> cache;
+    Node root;
+    std::vector<Node*> node_of;   // trie node of a cached block, else nullptr
+    std::vector<Node*> evicted;   // nodes that lost their block in this operation
     std::unordered_map<int64_t, Seq> seqs;
+
+    ~pa_block_manager() { free_kids(&root); }
+    static void free_kids(Node* n) {
+        for (auto& kv : n->kids) {
+            free_kids(kv.second);
+            delete kv.second;
+        }
+        n->kids.clear();
+    }
 
     int num_free() const { return (int)free_q.size() + n_evictable; }
 
@@ -86,15 +100,45 @@ struct pa_block_manager {
         } else {
             b = head;
             lru_remove(b);
-            cache.erase(key_of[b]);
-            cached[b] = 0;
+            Node* n = node_of[b];
+            n->block = -1;
+            node_of[b] = nullptr;
+            evicted.push_back(n);
         }
         ref[b] = 1;
         return b;
     }
     void drop(int32_t b) {
         if (--ref[b] == 0) {
-            if (cached[b]) lru_push(b); else free_q.push_back(b);
+            if (node_of[b]) lru_push(b); else free_q.push_back(b);
+        }
+    }
+    // The child of n for block content t, created if missing.
+    Node* child(Node* n, const BlockToks& t) {
+        auto it = n->kids.find(t);
+        if (it != n->kids.end()) return it->second;
+        Node* c = new Node;
+        c->parent = n;
+        c->toks = t;
+        n->kids.emplace(t, c);
+        return c;
+    }
+    // End of an operation: drop the trie nodes that now hold no block and
+    // lead to none (deferred so that no node goes away while an operation
+    // holds it).
+    // (A work set, not a walk up from each node: two evicted nodes may lie
+    // on one path, and removing the lower one can remove the upper one.)
+    void prune() {
+        std::set<Node*> work(evicted.begin(), evicted.end());
+        evicted.clear();
+        while (!work.empty()) {
+            Node* n = *work.begin();
+            work.erase(work.begin());
+            if (n == &root || n->block >= 0 || !n->kids.empty()) continue;
+            Node* p = n->parent;
+            p->kids.erase(n->toks);
+            delete n;
+            work.insert(p);
         }
     }
 };
@@ -113,8 +157,7 @@ pa_block_manager* pa_bm_create(int num_blocks, int prefix_cache) {
         bm->next.assign(num_blocks, -1);
         bm->in_lru.assign(num_blocks, 0);
         bm->ref.assign(num_blocks, 0);
-        bm->cached.assign(num_blocks, 0);
-        bm->key_of.assign(num_blocks, 0);
+        bm->node_of.assign(num_blocks, nullptr);
     } catch (...) {
         delete bm;
         return nullptr;
@@ -137,15 +180,16 @@ int pa_bm_add(pa_block_manager* bm, int64_t seq, const int64_t* tokens, int n_to
     try {
         const int nblk = (n_tokens + kBlock - 1) / kBlock;
         const int full = n_tokens / kBlock;
-        std::vector<uint64_t> keys(full);
-        uint64_t h = 0;
-        for (int i = 0; i < full; ++i) keys[i] = h = chain_hash(h, tokens + (size_t)i * kBlock);
+        // the longest cached prefix of whole blocks: walk the trie while each
+        // block's node holds a cached block
         std::vector<int32_t> hits;
         if (bm->prefix_cache) {
+            const Node* cur = &bm->root;
             for (int i = 0; i < full; ++i) {
-                auto it = bm->cache.find(keys[i]);
-                if (it == bm->cache.end()) break;
-                hits.push_back(it->second);
+                auto it = cur->kids.find(block_toks(tokens + (size_t)i * kBlock));
+                if (it == cur->kids.end() || it->second->block < 0) break;
+                cur = it->second;
+                hits.push_back(cur->block);
             }
         }
         int revived = 0;
@@ -155,24 +199,33 @@ int pa_bm_add(pa_block_manager* bm, int64_t seq, const int64_t* tokens, int n_to
         Seq s;
         s.table.reserve(nblk);
         s.n = n_tokens;
-        for (int32_t b : hits) {
+        Node* cur = &bm->root;
+        for (size_t i = 0; i < hits.size(); ++i) {
+            const int32_t b = hits[i];
             if (bm->ref[b] == 0) bm->lru_remove(b);
             ++bm->ref[b];
             s.table.push_back(b);
+            cur = bm->node_of[b];
         }
         for (int i = (int)hits.size(); i < nblk; ++i) {
             const int32_t b = bm->take();
             s.table.push_back(b);
-            if (bm->prefix_cache && i < full && !bm->cache.count(keys[i])) {
-                bm->cache.emplace(keys[i], b);
-                bm->key_of[b] = keys[i];
-                bm->cached[b] = 1;
+            // a full prompt block is cached under its prefix unless a block
+            // is already cached there
+            if (bm->prefix_cache && i < full) {
+                cur = bm->child(cur, block_toks(tokens + (size_t)i * kBlock));
+                if (cur->block < 0) {
+                    cur->block = b;
+                    bm->node_of[b] = cur;
+                }
             }
         }
         bm->seqs.emplace(seq, std::move(s));
+        bm->prune();
         if (cached_tokens) *cached_tokens = (int)hits.size() * kBlock;
         return PA_OK;
     } catch (...) {
+        bm->prune();
         return PA_ERR_INVALID_ARG;
     }
 }
@@ -198,8 +251,10 @@ int pa_bm_append(pa_block_manager* bm, int64_t seq, int32_t* cow_src, int32_t* c
             *cow_dst = dst;
         }
     } catch (...) {
+        bm->prune();
         return PA_ERR_INVALID_ARG;
     }
+    bm->prune();
     ++s.n;
     return PA_OK;
 }

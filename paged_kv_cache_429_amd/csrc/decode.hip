@@ -83,9 +83,9 @@ void decode_kernel(DecodeParams p) {
     const int32_t* trow = p.tables + (size_t)u.s * p.max_blocks;
     const bool ids_early = FMT != FMT_F32 && p.prefix_ts == 0 && p.window == 0;
     int wave_ids = 0;
-    if (ids_early) {
+    if (ids_early) {  // entries as stored; checked once the partition's extent is known
         const int first = u.part * p.pb;  // < blocks of a sequence at ctx_cap <= max_blocks
-        wave_ids = load_wave_ids(trow, first, min(p.max_blocks - first, kMaxPartitionBlocks), p.num_blocks);
+        wave_ids = load_wave_ids_raw(trow, first, min(p.max_blocks - first, kMaxPartitionBlocks));
     }
     u.ctx = min(p.ctx[u.s], p.ctx_cap);
     if (u.ctx <= 0) {
@@ -135,16 +135,29 @@ void decode_kernel(DecodeParams p) {
         __syncthreads();
         f32_wave<D>(p, u, trow, st, qs);
     } else {
-        if (!ids_early) wave_ids = load_wave_ids(trow, u.b_begin, u.b_end - u.b_begin, p.num_blocks);
+        if (ids_early) {
+            wave_ids = check_wave_ids(wave_ids, p.tables, trow, u.b_begin, u.b_end - u.b_begin, p.num_blocks);
+        } else {
+            wave_ids = load_wave_ids(p.tables, trow, u.b_begin, u.b_end - u.b_begin, p.num_blocks);
+        }
         mfma_wave<D, FMT>(p, u, wave_ids, st);
     }
     epilogue<D, F32OUT>(p, u, st, scratch, kCap);
 }
 
-// Workspace: a fixed-size region of arrival counters at offset 0, then the
+hipError_t take_bad_id_decode(BadIdRecord* out) {
+    const BadIdRecord zero{};
+    hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_bad_ids), sizeof(BadIdRecord), 0, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && out->flag)
+        e = hipMemcpyToSymbol(HIP_SYMBOL(g_bad_ids), &zero, sizeof zero, 0, hipMemcpyHostToDevice);
+    return e;
+}
+
+// Workspace: a fixed-size region of arrival words at offset 0, then the
 // partial accumulators and (max, sum) pairs. Because the counter region
-// never moves or shrinks, calls of any shape can share one workspace: the
-// counters stay zero between calls and partial data never lands on them.
+// never moves or shrinks, calls of any shape can share one workspace:
+// partial data never lands on the arrival words, and those are tagged with
+// each call's epoch, so no call depends on what an earlier one left there.
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // The prefix pass adds kpmax partial slots per (sequence, query head) and
@@ -158,11 +171,11 @@ size_t decode_workspace_bytes(int num_seqs, int n_heads, int n_kv, int d, int pm
 }
 
 void decode_workspace_carve(void* ws, int num_seqs, int n_heads, int n_kv, int d, int pmax, int kpmax,
-                            float** part_acc, float** part_ml, int** counters, int** plan) {
+                            float** part_acc, float** part_ml, unsigned long long** counters, int** plan) {
     (void)n_kv;
     const size_t rows = (size_t)num_seqs * n_heads * (pmax + kpmax);
     char* b = static_cast<char*>(ws);
-    *counters = reinterpret_cast<int*>(b);
+    *counters = reinterpret_cast<unsigned long long*>(b);
     b += kCounterBytes;
     *part_acc = reinterpret_cast<float*>(b);
     b += align256(rows * d * sizeof(float));

@@ -286,6 +286,14 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint8_t* __restri
     if (threadIdx.x == 0) xor_out[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
 }
 
+hipError_t take_bad_id_kvops(BadIdRecord* out) {
+    const BadIdRecord zero{};
+    hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_bad_ids), sizeof(BadIdRecord), 0, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && out->flag)
+        e = hipMemcpyToSymbol(HIP_SYMBOL(g_bad_ids), &zero, sizeof zero, 0, hipMemcpyHostToDevice);
+    return e;
+}
+
 hipError_t launch_read_probe(const void* buf, long buf_tiles, long n_tiles, int tile_bytes, const int32_t* order,
                              uint32_t* xor_out, int grid, hipStream_t stream) {
     hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)grid), dim3(256), 0, stream,

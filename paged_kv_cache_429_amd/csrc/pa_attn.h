@@ -38,18 +38,29 @@ struct Unit {
 // Block ids of a partition, spread over its four waves. Wave w visits the
 // pairs w, w + 4, w + 8, ..., so lane 2n + e of its id register holds the id
 // of block 2 (w + 4n) + e of the partition: 64 lanes cover the wave's share
-// of up to 256 blocks. Blocks at or past nb, and ids outside the pool, read
-// as 0 (never dereferenced past the pool).
-__device__ __forceinline__ int load_wave_ids(const int32_t* trow, int first, int nb, int num_blocks) {
+// of up to 256 blocks. trow is the sequence's row of the table array
+// `tables`. Blocks at or past nb read as 0; ids outside the pool read as 0
+// and are recorded (never dereferenced past the pool).
+__device__ __forceinline__ int wave_id_slot() {
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    const int j = 2 * (w + kWaves * (lane >> 1)) + (lane & 1);
-    int id = 0;
-    if (j < nb) {
-        id = trow[first + j];
-        if ((unsigned)id >= (unsigned)num_blocks) id = 0;
-    }
-    return id;
+    return 2 * (w + kWaves * (lane >> 1)) + (lane & 1);
+}
+// The table entries of load_wave_ids as stored (unchecked; 0 past nb).
+__device__ __forceinline__ int load_wave_ids_raw(const int32_t* trow, int first, int nb) {
+    const int j = wave_id_slot();
+    return j < nb ? trow[first + j] : 0;
+}
+// Entries of load_wave_ids_raw(trow, first, >= nb) checked against the pool
+// for the nb blocks the partition uses (0 past them).
+__device__ __forceinline__ int check_wave_ids(int raw, const int32_t* tables, const int32_t* trow, int first, int nb,
+                                              int num_blocks) {
+    const int j = wave_id_slot();
+    return j < nb ? checked_id(raw, (long)(trow - tables) + first + j, num_blocks) : 0;
+}
+__device__ __forceinline__ int load_wave_ids(const int32_t* tables, const int32_t* trow, int first, int nb,
+                                             int num_blocks) {
+    return check_wave_ids(load_wave_ids_raw(trow, first, nb), tables, trow, first, nb, num_blocks);
 }
 
 // Id of block e (0 or 1) of pair k, one of this wave's pairs (k = w + 4n,
@@ -719,13 +730,11 @@ __device__ __forceinline__ void mfma_wave(const DecodeParams& p, const Unit& u, 
 // -----------------------------------------------------------------------------
 // Physical id of block (b_begin + j) for j in a 64-block window starting at
 // `base`: lane l holds the id of block base + l; out-of-range ids become 0.
-__device__ __forceinline__ int load_ids(const int32_t* trow, int first, int count, int num_blocks) {
+__device__ __forceinline__ int load_ids(const int32_t* tables, const int32_t* trow, int first, int count,
+                                        int num_blocks) {
     const int lane = threadIdx.x & 63;
     int id = 0;
-    if (lane < count) {
-        id = trow[first + lane];
-        if ((unsigned)id >= (unsigned)num_blocks) id = 0;
-    }
+    if (lane < count) id = checked_id(trow[first + lane], (long)(trow - tables) + first + lane, num_blocks);
     return id;
 }
 
@@ -757,7 +766,8 @@ __device__ __forceinline__ void f32_wave(const DecodeParams& p, const Unit& u, c
     for (int j = wave; j < nb_part; j += kWaves) {
         if ((j >> 6) != window) {  // ids of the next 64 blocks
             window = j >> 6;
-            my_id = load_ids(trow, u.b_begin + (window << 6), min(64, nb_part - (window << 6)), p.num_blocks);
+            my_id = load_ids(p.tables, trow, u.b_begin + (window << 6), min(64, nb_part - (window << 6)),
+                             p.num_blocks);
         }
         const int id = readlane(my_id, j & 63);
         const size_t toff = ((size_t)id * p.n_kv + u.kvh) * TILE;
@@ -1082,14 +1092,27 @@ __device__ __forceinline__ void merge_waves_prefix_store(const DecodeParams& p, 
 }
 
 // Count one partition of (sequence s, KV head kvh) as arrived; true for the
-// last of its nparts partitions, which then re-arms the counter (zero
-// between calls). Called by one thread after every thread's partial stores
-// have reached the coherence point.
+// last of its nparts partitions. The arrival word holds the epoch of the
+// call that last counted in it and that call's arrivals: a word of another
+// epoch (left by an earlier call, complete or not) counts as none. The last
+// arrival leaves its epoch with a count of zero, so a replay of the same
+// launch (same epoch) starts from zero too. Called by one thread after
+// every thread's partial stores have reached the coherence point. The
+// compare-and-swap is retried only when another arrival changed the word,
+// so it ends after at most nparts tries.
 __device__ __forceinline__ bool arrive(const DecodeParams& p, int s, int kvh, int nparts) {
-    int* cnt = p.counters + (size_t)s * p.n_kv + kvh;
-    const int before = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = (before == nparts - 1);
-    if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned long long* w = p.counters + (size_t)s * p.n_kv + kvh;
+    const unsigned long long tag = (unsigned long long)p.epoch << 32;
+    unsigned long long old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool last;
+    while (true) {
+        const unsigned long long n = (old >> 32) == (unsigned long long)p.epoch ? (old & 0xffffffffull) : 0ull;
+        last = n + 1 >= (unsigned long long)nparts;
+        const unsigned long long want = last ? tag : (tag | (n + 1));
+        if (__hip_atomic_compare_exchange_strong(w, &old, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+            break;
+    }
     return last;
 }
 
@@ -1185,9 +1208,10 @@ __device__ __forceinline__ bool group_shares(const DecodeParams& p, int s0, int 
 // SIMD and keep the per-wave layout of the per-sequence path (up to 256).
 struct SpanIds {
     int lo, hi;
-    __device__ __forceinline__ void load(const int32_t* trow, int first, int nb, int num_blocks) {
-        lo = load_ids(trow, first, min(nb, 64), num_blocks);
-        hi = nb > 64 ? load_ids(trow, first + 64, nb - 64, num_blocks) : 0;
+    __device__ __forceinline__ void load(const int32_t* tables, const int32_t* trow, int first, int nb,
+                                         int num_blocks) {
+        lo = load_ids(tables, trow, first, min(nb, 64), num_blocks);
+        hi = nb > 64 ? load_ids(tables, trow, first + 64, nb - 64, num_blocks) : 0;
     }
     // id of block e of pair k (wave-uniform k, 2k + e < 128)
     __device__ __forceinline__ int get(int k, int e) const {
@@ -1200,8 +1224,9 @@ struct SpanIds {
 
 struct WaveIds {
     int r;
-    __device__ __forceinline__ void load(const int32_t* trow, int first, int nb, int num_blocks) {
-        r = load_wave_ids(trow, first, nb, num_blocks);
+    __device__ __forceinline__ void load(const int32_t* tables, const int32_t* trow, int first, int nb,
+                                         int num_blocks) {
+        r = load_wave_ids(tables, trow, first, nb, num_blocks);
     }
     __device__ __forceinline__ int get(int k, int e) const { return pair_id(r, k, e); }
 };
@@ -1246,7 +1271,7 @@ __device__ __forceinline__ void shared_unit(const DecodeParams& p, int unit, Wav
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
         const int32_t* trow = p.tables + (size_t)(s0 + i) * p.max_blocks;
-        my_id[i].load(trow, b, nbp[i], p.num_blocks);
+        my_id[i].load(p.tables, trow, b, nbp[i], p.num_blocks);
     }
 
     u32x4 qop[CS][M::KSTEPS];

@@ -5,7 +5,34 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pa_internal.h"
+
 namespace pa {
+
+// The first block-table entry outside [0, num_blocks) that a kernel of this
+// source file met on this device since the host last took the record (the
+// kernels read such an entry as block 0). Taken by take_bad_id_*.
+static __device__ BadIdRecord g_bad_ids;
+
+// Record entry `idx` of a block-table array holding the out-of-range id
+// `id`, unless a record is already held. Runs only for such an entry.
+__device__ __noinline__ void note_bad_id(long idx, int id) {
+    if (atomicCAS(&g_bad_ids.flag, 0, 1) == 0) {
+        g_bad_ids.idx_hi = (int)(idx >> 32);
+        g_bad_ids.idx_lo = (unsigned)idx;
+        g_bad_ids.id = id;
+    }
+}
+
+// Block id `id` read from entry `idx` of the table array, or 0 (recorded)
+// when it lies outside the pool.
+__device__ __forceinline__ int checked_id(int id, long idx, int num_blocks) {
+    if ((unsigned)id >= (unsigned)num_blocks) {
+        note_bad_id(idx, id);
+        id = 0;
+    }
+    return id;
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -27,6 +27,12 @@ __host__ __device__ inline int num_parts(int nblk, int pb) {
 __host__ __device__ inline int part_end(int nblk, int pb, int part, int nparts) {
     return part + 1 == nparts ? nblk : (part + 1) * pb;
 }
+// Most blocks a partition can hold at pb blocks per partition (the last
+// partition's absorbed remainder included).
+__host__ __device__ inline int max_partition_blocks(int pb) {
+    const int thr = pb / kAbsorbDiv < kMaxPartitionBlocks - pb ? pb / kAbsorbDiv : kMaxPartitionBlocks - pb;
+    return pb + thr;
+}
 
 // Prefix pass ("jovanaeducation" guide a2-inf-2, section "Prefix caching";
 // "KV cache, GQA, paging and continuous batching", section
@@ -60,7 +66,8 @@ struct DecodeParams {
     void* out;
     float* part_acc;    // [num_seqs][n_heads][pslots][d]   (unnormalised)
     float* part_ml;     // [num_seqs][n_heads][pslots][2]   (max, sum) in log2 units
-    int* counters;      // [num_seqs][n_kv] partitions arrived (zero between calls)
+    unsigned long long* counters;  // [num_seqs][n_kv] arrival words: epoch << 32 | partitions arrived
+    unsigned epoch;     // this call's epoch (never 0); a word of another epoch counts as 0 arrivals
     int max_blocks;     // table row stride
     int ctx_cap;        // min(max_context_len, 16 * max_blocks)
     int num_seqs;
@@ -80,15 +87,23 @@ struct DecodeParams {
 };
 
 // Bytes of the arrival-counter region at the start of a decode workspace:
-// one int32 per (sequence, KV head), so num_seqs * n_kv_heads <= 262144.
-constexpr size_t kCounterBytes = (size_t)1 << 20;
-constexpr long kMaxCounterPairs = (long)(kCounterBytes / sizeof(int));
+// one 64-bit word per (sequence, KV head), so num_seqs * n_kv_heads <=
+// 262144. A word holds the epoch of the call that last counted in it (high
+// half) and the partitions of that call that have arrived (low half); every
+// call has an epoch of its own, so whatever a word holds from an earlier
+// call (one that completed, or one whose launch died midway) counts as zero
+// arrivals, and the region needs no initialisation.
+constexpr size_t kCounterBytes = (size_t)2 << 20;
+constexpr long kMaxCounterPairs = (long)(kCounterBytes / sizeof(unsigned long long));
+
+// A fresh epoch for a decode call (process-wide counter, skipping 0).
+unsigned next_epoch();
 
 // Workspace bytes for the arrival counters and split-context partials (0
 // when pmax == 1).
 size_t decode_workspace_bytes(int num_seqs, int n_heads, int n_kv, int d, int pmax, int kpmax);
 void decode_workspace_carve(void* ws, int num_seqs, int n_heads, int n_kv, int d, int pmax, int kpmax,
-                            float** part_acc, float** part_ml, int** counters, int** plan);
+                            float** part_acc, float** part_ml, unsigned long long** counters, int** plan);
 
 // fmt: 0 fp32, 1 bf16, 2 int8, 3 int4. Launches the decode kernel on
 // `stream`.
@@ -127,6 +142,20 @@ hipError_t launch_prefill(const PrefillParams& p, int d, int fmt, hipStream_t st
 // num_seqs, tables, ctx, ctx_cap, q as for the decode; writes the tiles'
 // plan entries and the prefix partials in slots 0 .. prefix_parts() - 1.
 hipError_t launch_prefix(const PrefillParams& p, hipStream_t stream);
+
+// Block-table entries outside [0, num_blocks) met by a kernel are read as
+// block 0 and recorded: the first one per device and per source file, as
+// (flag, table index high, table index low, id). read_*_bad_id copies the
+// record of that file's kernels to the host and clears it (synchronous).
+struct BadIdRecord {
+    int flag;
+    int idx_hi;
+    unsigned idx_lo;
+    int id;
+};
+hipError_t take_bad_id_decode(BadIdRecord* out);
+hipError_t take_bad_id_prefill(BadIdRecord* out);
+hipError_t take_bad_id_kvops(BadIdRecord* out);
 
 hipError_t launch_quantize(const void* src, void* codes, uint16_t* scales, const int32_t* block_ids, int n_ids,
                            int num_blocks, int n_kv, int d, int bits, int kind, hipStream_t stream);

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p, int 
     auto fetch = [&](int k) {
         if (((2 * k) >> 6) != window) {
             window = (2 * k) >> 6;
-            my_id = load_ids(trow, window << 6, min(64, nblk - (window << 6)), p.num_blocks);
+            my_id = load_ids(p.tables, trow, window << 6, min(64, nblk - (window << 6)), p.num_blocks);
         }
         const int j0 = (2 * k) & 63;
         const int id0 = readlane(my_id, j0);
@@ -420,7 +420,7 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
     auto prefetch = [&](int st, uint8_t* buf) {
         if ((st * kStageBlocks) >> 6 != win) {  // ids of the next 64 blocks
             win = (st * kStageBlocks) >> 6;
-            win_id = load_ids(trow, win << 6, min(64, nblk - (win << 6)), p.num_blocks);
+            win_id = load_ids(p.tables, trow, win << 6, min(64, nblk - (win << 6)), p.num_blocks);
         }
 #pragma unroll
         for (int j = 0; j < KLD; ++j) {
@@ -648,6 +648,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(PrefillParams pp)
     p.pmax = 1;
     p.pslots = 1;
     p.scale_log2 = pp.scale_log2;
+    p.tables = pp.tables;
 
     Unit u;
     u.s = q0 + i;  // output / query row
@@ -670,6 +671,14 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(PrefillParams pp)
     __syncthreads();
     f32_wave<D>(p, u, pp.tables + (size_t)s * pp.max_blocks, st, qs);
     epilogue<D, true>(p, u, st, reinterpret_cast<float*>(&st), (int)(sizeof(st) / sizeof(float)));
+}
+
+hipError_t take_bad_id_prefill(BadIdRecord* out) {
+    const BadIdRecord zero{};
+    hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_bad_ids), sizeof(BadIdRecord), 0, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && out->flag)
+        e = hipMemcpyToSymbol(HIP_SYMBOL(g_bad_ids), &zero, sizeof zero, 0, hipMemcpyHostToDevice);
+    return e;
 }
 
 template <int D, int FMT, int C>

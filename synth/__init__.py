@@ -17,6 +17,7 @@ from .gen import (  # noqa: F401
     make_prefill_case,
     make_probe_case,
     make_prefill_probe_case,
+    make_prefix_probe_case,
     permute_pool,
     poison_unused,
     private_twin,

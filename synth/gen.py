@@ -432,6 +432,47 @@ def make_probe_case(n_heads, n_kv, d, dtype, ctx, seed, *, pool_factor=1.25, mag
     return out
 
 
+def make_prefix_probe_case(n_heads, n_kv, d, dtype, prefix_tokens, tails, seed, *, shared_pos, tail_magnet):
+    """Decode probe over a shared prefix: every sequence's table points its
+    first prefix_tokens / 16 blocks at the same physical blocks, followed by
+    a private tail of tails[s] tokens. K is zero except a 'shared' magnet
+    40*e0 at prefix position shared_pos (seen by every sequence) and, for
+    each sequence with tail_magnet[s], a 'tail' magnet 80*e0 at a seeded
+    position of its tail; every query is 40*e0. Scores are then 0, 1600 and
+    3200 (exact), i.e. gaps of at least 1600/sqrt(d) >= 141 between the
+    largest score and every other, so every other softmax weight underflows
+    to 0 in float32: the output is V at the sequence's tail magnet if it
+    has one, else V at shared_pos, exactly. V encodes each slot's offset,
+    KV head and physical block (see _probe_digits)."""
+    assert prefix_tokens % BLOCK_SIZE == 0 and 0 <= shared_pos < prefix_tokens
+    tails = np.asarray(tails, dtype=np.int64)
+    assert (tails >= 1).all() and len(tail_magnet) == len(tails)
+    ctx = prefix_tokens + tails
+    base = make_decode_case(n_heads, n_kv, d, "f32", ctx, seed, shared_prefix_tokens=prefix_tokens)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 5])))
+    S = base.num_seqs
+    nslots = base.num_blocks * BLOCK_SIZE
+    k = np.zeros((nslots, n_kv, d), dtype=np.float32)
+
+    def slot(s, t):
+        return int(base.block_tables[s, t // BLOCK_SIZE]) * BLOCK_SIZE + t % BLOCK_SIZE
+
+    k[slot(0, shared_pos), :, 0] = 40.0
+    tstar = np.full(S, shared_pos, dtype=np.int64)
+    for s in range(S):
+        if tail_magnet[s]:
+            tstar[s] = prefix_tokens + int(g.integers(0, int(tails[s])))
+            k[slot(s, int(tstar[s])), :, 0] = 80.0
+    v = _probe_digits(nslots, n_kv, d)
+    q = np.zeros((S, n_heads, d), dtype=np.float32)
+    q[:, :, 0] = 40.0
+    if dtype == "bf16":
+        q, k, v = f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+    out = replace(base, dtype=dtype, q=q, k_slots=k, v_slots=v, name="prefix_probe")
+    out.extra = dict(tstar=tstar)
+    return out
+
+
 def make_prefill_probe_case(n_heads, n_kv, d, dtype, ctx, q_lens, seed):
     """Causal prefill probe: key t is (t // 64, t % 64, 0, ...) and every query
     is (2**17, 2**11, 0, ...), so scores are exact integers strictly

@@ -104,7 +104,7 @@ def test_workspace_size(B):
     n = L.paged_attn_decode_workspace_size(4, 8, 2, 128, 4096, 16)          # 16 partitions
     rows = 4 * 8 * 16
     al = lambda x: (x + 255) // 256 * 256
-    assert n == (1 << 20) + al(rows * 128 * 4) + al(rows * 2 * 4)   # counters, partial acc, (m, l)
+    assert n == (2 << 20) + al(rows * 128 * 4) + al(rows * 2 * 4)   # arrival words, partial acc, (m, l)
     assert L.paged_attn_decode_workspace_size(4, 8, 2, 128, 4096, 3) == 0   # invalid partition size
 
 
@@ -165,7 +165,7 @@ def _parts(nblk, pb):
 def test_partition_plan_through_workspace_size(B, S, H, kv, mcl, pb_want):
     """The library's automatic partition size, read back through the
     workspace it asks for (a device-free call; 256 compute units assumed
-    without a GPU): 1 MiB of counters plus S * H * pmax rows of d + 2 floats
+    without a GPU): 2 MiB of arrival words plus S * H * pmax rows of d + 2 floats
     (each part 256-byte aligned), pmax being the partitions of a sequence at
     max_context_len, plus the prefix pass's slots where it applies."""
     L = B.lib()
@@ -177,7 +177,7 @@ def test_partition_plan_through_workspace_size(B, S, H, kv, mcl, pb_want):
         pmax = _parts(-(-mcl // 16), pb_want)
         al = lambda x: (x + 255) // 256 * 256
         rows = S * H * pmax
-        want = (1 << 20) + al(rows * d * 4) + al(rows * 2 * 4) if pmax > 1 else 0
+        want = (2 << 20) + al(rows * d * 4) + al(rows * 2 * 4) if pmax > 1 else 0
         assert got == want
 
 
@@ -188,7 +188,7 @@ def test_workspace_when_no_sequence_splits(B):
     L = B.lib()
     assert L.paged_attn_decode_workspace_size(128, 16, 8, 128, 4096, 256) == 0      # G = 2, 256 rows
     assert L.paged_attn_decode_workspace_size(256, 48, 16, 128, 4096, 256) == 0     # G = 3
-    assert L.paged_attn_decode_workspace_size(256, 32, 8, 128, 4096, 256) > (1 << 20)  # G = 4, 1024 rows
+    assert L.paged_attn_decode_workspace_size(256, 32, 8, 128, 4096, 256) > (2 << 20)  # G = 4, 1024 rows
     assert L.paged_attn_decode_workspace_size(256, 32, 8, 64, 4096, 256) == 0       # d 64: no pass
 
 

@@ -241,6 +241,49 @@ def test_scheduler_matches_model(B, seed, num_blocks):
     _check_model_invariants(m)
 
 
+def test_prefix_cache_is_exact_per_prefix(B):
+    """A block whose tokens equal a cached block's, under a different
+    earlier block, is not a hit; the same two blocks under the same earlier
+    block are (the cache is keyed by the whole prefix, compared token by
+    token)."""
+    x, y, z = [1] * 16, [2] * 16, [3] * 16
+    for bm, name in ((B.BlockManager(16), "c++"), (M.BlockManager(16), "model")):
+        assert bm.add(1, x + y + [5]) == 0
+        assert bm.add(2, z + y + [5]) == 0, name
+        assert bm.add(3, x + y + [6]) == 32, name
+        assert bm.add(4, z + y) == 32, name
+
+
+@pytest.mark.parametrize("seed", [20, 21])
+def test_manager_matches_model_repeated_blocks(B, seed):
+    """Prompts over a two-token alphabet in runs of whole blocks, so the same
+    block contents recur under many different prefixes."""
+    g = np.random.default_rng(seed)
+    blocks = [[int(t)] * 16 for t in range(2)] + [list(g.integers(0, 2, 16)) for _ in range(2)]
+    bm, m = B.BlockManager(48, True), M.BlockManager(48, True)
+    live, next_id = [], 0
+    for step in range(400):
+        if not live or g.random() < 0.5:
+            toks = sum((blocks[int(i)] for i in g.integers(0, len(blocks), int(g.integers(0, 6)))), [])
+            toks += list(g.integers(0, 2, int(g.integers(0, 20))))
+            try:
+                want = m.add(next_id, toks)
+            except M.NoBlocks:
+                with pytest.raises(B.PagedAttnError, match="free KV blocks"):
+                    bm.add(next_id, toks)
+            else:
+                assert bm.add(next_id, toks) == want
+                live.append(next_id)
+            next_id += 1
+        else:
+            s = live.pop(int(g.integers(len(live))))
+            m.release(s)
+            bm.release(s)
+        _compare(bm, m, live)
+    _check_model_invariants(m)
+    bm.close()
+
+
 def test_manager_rejects_bad_arguments(B):
     L = B.lib()
     assert not L.pa_bm_create(0, 1) and not L.pa_bm_create(4, 2)

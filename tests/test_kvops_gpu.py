@@ -114,27 +114,44 @@ def test_quantized_decode_parity(lib, bits):
     assert_close(got, ref, "bf16", f"int{bits}")
 
 
-@pytest.mark.parametrize("bits", [8, 4])
-def test_workload4_quantized_sampled(lib, bits):
+@pytest.fixture(scope="module")
+def workload4():
+    return make_config_case(4)
+
+
+def _oracle_dequantized(slots, bits, chunk_blocks=1024):
+    """float64 values of the oracle's codes for a bf16 slot-form pool. Tiles
+    are quantized independently, so chunks of blocks go to the oracle
+    separately, on a thread pool (NumPy releases the GIL in these loops)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    out = np.empty(slots.shape, dtype=np.float64)
+    step = chunk_blocks * 16
+
+    def one(lo):
+        x = bf16_bits_to_f32(slots[lo:lo + step])
+        if bits == B.PA_KV_FP8:
+            out[lo:lo + step] = oracle.dequantize_fp8(*oracle.quantize_tiles_fp8(x))
+        else:
+            out[lo:lo + step] = oracle.dequantize(*oracle.quantize_tiles(x, bits))
+
+    with ThreadPoolExecutor(min(16, len(os.sched_getaffinity(0)))) as ex:
+        list(ex.map(one, range(0, slots.shape[0], step)))
+    return out
+
+
+@pytest.mark.parametrize("bits", [8, 4, 264])  # 264: fp8 (e4m3)
+def test_workload4_quantized_full_batch(lib, workload4, bits):
     """The whole 128 x 8000 batch, in the launch configuration the benchmark
-    times (the partition plan depends on the batch), checked on sampled
-    sequences."""
-    c = make_config_case(4)
+    times, every sequence against the oracle on its own codes."""
+    c = workload4
     kc, vc, ks, vs = _quant_case(c, bits)
     got = dev_to_f64(gpu_decode(c, kp=kc, vp=vc, kv_bits=bits, k_scales=ks, v_scales=vs))
-    seqs = [0, 7, 64, 127]
-    used = np.unique(c.block_tables[seqs].ravel())
-    used = used[used >= 0]
-    # oracle quantizes only the blocks those sequences read
-    rows = (used[:, None] * 16 + np.arange(16)[None, :]).ravel()
-    kq, kqs = oracle.quantize_tiles(bf16_bits_to_f32(c.k_slots[rows]), bits)
-    vq, vqs = oracle.quantize_tiles(bf16_bits_to_f32(c.v_slots[rows]), bits)
-    kd = np.zeros(c.k_slots.shape, dtype=np.float64)
-    vd = np.zeros(c.v_slots.shape, dtype=np.float64)
-    kd[rows] = oracle.dequantize(kq, kqs)
-    vd[rows] = oracle.dequantize(vq, vqs)
-    ref = oracle_decode(c, seqs=seqs, k_slots=kd, v_slots=vd)
-    assert_close(got[seqs], ref[seqs], "bf16", f"workload4 int{bits}")
+    del kc, vc, ks, vs
+    kd = _oracle_dequantized(c.k_slots, bits)
+    vd = _oracle_dequantized(c.v_slots, bits)
+    ref = oracle_decode(c, k_slots=kd, v_slots=vd)
+    assert_close(got, ref, "bf16", f"workload4 kv_bits {bits}")
 
 
 @pytest.mark.parametrize("bits", [8, 4])

@@ -7,7 +7,8 @@ import torch
 import oracle
 from oracle import brute
 from synth import (make_config_case, make_decode_case, make_mixed_case, make_prefill_case,
-                   make_prefill_probe_case, make_probe_case, permute_pool, poison_unused, private_twin)
+                   make_prefill_probe_case, make_prefix_probe_case, make_probe_case, permute_pool, poison_unused,
+                   private_twin)
 from synth.gen import bf16_bits_to_f32
 
 
@@ -236,6 +237,30 @@ def test_retrieval_probe_negative_control():
     bad_tables[0, j] = c.block_tables[1, j]
     bad = oracle.paged_decode(f64(c, c.q), f64(c, c.k_slots), f64(c, c.v_slots), bad_tables, c.context_lens, n_kv=2)
     assert not np.array_equal(good[0], bad[0])
+
+
+@pytest.mark.parametrize("dtype,shared_pos", [("bf16", 0), ("bf16", 200), ("f32", 255)])
+def test_prefix_retrieval_probe(dtype, shared_pos):
+    """Shared-prefix probe: a sequence with a tail magnet returns V there,
+    the others V at the shared magnet (up to float64 weights below 1e-60 on
+    the other keys, which float32 flushes to 0); brute force agrees."""
+    tails = [1, 5, 16, 17, 40, 3]
+    c = make_prefix_probe_case(16, 4, 64, dtype, 256, tails, 19, shared_pos=shared_pos,
+                               tail_magnet=[1, 0, 1, 0, 1, 1])
+    out = run_decode(c)
+    v = f64(c, c.v_slots)
+    for s in range(c.num_seqs):
+        t = int(c.extra["tstar"][s])
+        assert (t == shared_pos) != bool([1, 0, 1, 0, 1, 1][s])
+        slot = c.block_tables[s, t // 16] * 16 + t % 16
+        for h in range(16):
+            np.testing.assert_allclose(out[s, h], v[slot, h // 4], rtol=0, atol=1e-40, err_msg=f"{s} {h}")
+    # every sequence points its first 16 blocks at the same physical blocks
+    assert (c.block_tables[:, :16] == c.block_tables[0, :16]).all()
+    q, k, vv = f64(c, c.q), f64(c, c.k_slots).tolist(), v.tolist()
+    for s in (0, 1):
+        ref = brute.decode_attention(q[s].tolist(), k, vv, c.block_tables[s].tolist(), int(c.context_lens[s]), 4)
+        np.testing.assert_allclose(out[s], np.array(ref), rtol=0, atol=1e-12)
 
 
 def test_prefill_vs_brute_force():

@@ -86,9 +86,14 @@ def test_prefill_q1_matches_decode(lib):
     assert_close(dev_to_f64(got), dev_to_f64(dec), "bf16", "q_len 1 vs decode")
 
 
-def test_workload5_chunk_sampled(lib):
+def test_workload5_chunk_rows(lib):
+    """The 2048-token chunk over 6000 cached tokens: the first and last row
+    of every 64-row workgroup tile (256 / G chunk tokens at G = 4), every row
+    of the first and last tiles and of one in the middle, against the
+    oracle."""
     pre, _ = make_mixed_case()
     got = dev_to_f64(gpu_prefill(pre))
-    rows = [0, 1, 15, 16, 17, 511, 1024, 1500, 2046, 2047]
+    rows = sorted({r for t in range(0, 2048, 64) for r in (t, t + 63)} | set(range(0, 64)) |
+                  set(range(1024, 1088)) | set(range(1984, 2048)))
     ref = oracle_prefill(pre, rows=rows)
     assert_close(got[rows], ref[rows], "bf16", "workload5 chunk")
