@@ -97,7 +97,9 @@ typedef enum pa_status {
     PA_ERR_INVALID_ARG = -1,  /* a pointer, size or shape is invalid            */
     PA_ERR_UNSUPPORTED = -2,  /* valid, but not a shape/format this build runs  */
     PA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required     */
-    PA_ERR_HIP = -4           /* a HIP runtime call failed                      */
+    PA_ERR_HIP = -4,          /* a HIP runtime call failed                      */
+    PA_ERR_SCRATCH = -7       /* paged_attn_decode_noalloc: the call needs more
+                                 scratch than its fixed device array holds      */
 } pa_status;
 
 typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
@@ -108,6 +110,8 @@ typedef enum pa_kv_kind { PA_KIND_K = 0, PA_KIND_V = 1 } pa_kv_kind;
 /* kv_bits code of OCP fp8 e4m3 pools (8 bits of storage per element). */
 #define PA_KV_FP8 264
 #define PA_DECODE_COUNTER_BYTES (2u << 20)
+/* Bytes of the fixed per-device scratch of paged_attn_decode_noalloc. */
+#define PA_DECODE_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /* Human-readable text of a status code (static storage). */
 const char* pa_error_string(int status);
@@ -204,6 +208,31 @@ int paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
                       int n_heads, int n_kv_heads, int d_head, int dtype, int kv_bits,
                       void* out, void* workspace, size_t workspace_bytes,
                       int partition_blocks, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * paged_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. The call allocates nothing (no hipMalloc,
+ * no hipFree, no allocating library routine): its scratch is a fixed
+ * device array of PA_DECODE_NOALLOC_SCRATCH_BYTES (64 MiB) that the library
+ * holds on each device it runs on until the process ends. Arguments and
+ * results as for paged_attn_decode (the caller still passes the inputs and
+ * the output). A call whose workspace, as paged_attn_decode_workspace_size()
+ * gives it, exceeds the array returns PA_ERR_SCRATCH before any device work
+ * (the 70B prefix-shared batch of 256 x 4500 tokens needs about 51 MiB).
+ * The first call on a device takes the array's device address
+ * (PA_ERR_HIP if that fails). The array keeps whatever the last call left;
+ * nothing in it needs to start at zero (arrival words are epoch-tagged).
+ * Every call on one device shares the array: calls that overlap on a device
+ * (different streams, or host threads, without ordering) race.
+ * ------------------------------------------------------------------------ */
+int paged_attn_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                              const uint16_t* k_scales, const uint16_t* v_scales,
+                              const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* context_lens, int max_context_len,
+                              int num_seqs, int num_blocks, int block_size,
+                              int n_heads, int n_kv_heads, int d_head, int dtype, int kv_bits,
+                              void* out, int partition_blocks, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Sliding-window decode ([IR] "The memory equation": sliding-window attention

@@ -25,6 +25,7 @@ BLOCK_SIZE = 16
 EXPORTS = (
     "pa_error_string", "pa_tile_bytes", "pa_kv_bytes_per_token", "pa_kv_cache_bytes",
     "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_decode_window", "paged_attn_prefill_chunk",
+    "paged_attn_decode_noalloc",
     "kv_quantize", "paged_kv_write", "pa_copy_blocks", "pa_hbm_read_probe", "pa_take_block_id_error",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_ref_count", "pa_bm_add", "pa_bm_append",
     "pa_bm_fork", "pa_bm_release", "pa_bm_num_tokens", "pa_bm_table",
@@ -57,6 +58,8 @@ def _declare(lib):
     lib.paged_attn_decode_window.restype = i
     lib.paged_attn_decode_window.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, i, i, i, vp, vp, sz, i, i,
                                              vp]
+    lib.paged_attn_decode_noalloc.restype = i
+    lib.paged_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, i, i, i, vp, i, vp]
     lib.paged_attn_prefill_chunk.restype = i
     lib.paged_attn_prefill_chunk.argtypes = [vp, vp, i, i, vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, i, i, i,
                                              vp, vp]

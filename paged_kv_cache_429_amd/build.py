@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedattn.so")
-SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "kvops.hip", "block_manager.cpp"]
+SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "kvops.hip", "block_manager.cpp", "noalloc.hip"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 

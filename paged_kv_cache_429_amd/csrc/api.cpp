@@ -141,6 +141,7 @@ const char* pa_error_string(int status) {
         case PA_ERR_HIP: return "HIP runtime error";
         case -5: return "not enough free KV blocks";
         case -6: return "unknown (or already used) sequence id";
+        case PA_ERR_SCRATCH: return "the call needs more scratch than the no-allocation entry point holds";
         default: return "unknown status";
     }
 }

@@ -40,7 +40,7 @@ def test_exports_every_declared_function(B):
 
 def test_error_strings(B):
     L = B.lib()
-    for code in (0, -1, -2, -3, -4, 7):
+    for code in (0, -1, -2, -3, -4, -7, 7):
         assert L.pa_error_string(code)
 
 
@@ -87,11 +87,24 @@ def test_decode_rejects_on_host(B, over, code):
 
 
 def test_decode_counter_capacity(B):
-    """One int32 arrival counter per (sequence, KV head) lives in a fixed
-    1 MiB region: larger split batches are rejected on the host."""
+    """One 64-bit arrival word per (sequence, KV head) lives in a fixed
+    2 MiB region: larger split batches are rejected on the host."""
     ws = 1 << 40  # never dereferenced: the call returns before any device work
     assert _decode(B, ns=262144 // 8 + 1, Hkv=8, H=32, mb=256, mcl=4096, ws=ws, wsb=1 << 40) == -2
     assert _decode(B, ns=262144 // 8 + 1, Hkv=8, H=32, mb=256, mcl=4096, ws=None, wsb=0) == -2
+
+
+def test_noalloc_rejects_oversized_batches_on_host(B):
+    """paged_attn_decode_noalloc checks the scratch the call needs against its
+    fixed 64 MiB array before any device work: 512 sequences of the 70B
+    prefix-shared shape (about 67 MiB) are rejected with PA_ERR_SCRATCH."""
+    L = B.lib()
+    one = ctypes.c_void_p(1)  # never dereferenced
+    need = L.paged_attn_decode_workspace_size(512, 64, 8, 128, 4500, 0)
+    assert need > 64 << 20 > L.paged_attn_decode_workspace_size(256, 64, 8, 128, 4500, 0)
+    assert L.paged_attn_decode_noalloc(one, one, one, None, None, one, 282, one, 4500, 512, 100000, 16, 64, 8, 128,
+                                       1, 16, one, 0, None) == -7
+    assert b"scratch" in L.pa_error_string(-7)
 
 
 def test_decode_empty_batch_is_noop(B):
