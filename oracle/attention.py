@@ -24,9 +24,11 @@ at absolute position ctx - q_len + i and attends to keys 0..position
 (inclusive).
 
 Sliding window ([IR] "The memory equation" lists sliding-window attention
-among the ways to shrink the cache, with no formula): read as the query at
-position p attending only the last W tokens, keys p - W + 1 .. p, so W = 1
-is the token itself and W >= p + 1 is full attention.
+among the ways to shrink the cache, with no formula; [TAI] "The KV cache"
+names sliding-window layers): read as the query at position p attending only
+the last W tokens, keys p - W + 1 .. p, so W = 1 is the token itself and
+W >= p + 1 is full attention. The same rule holds for the decode's single
+query and for every row of a prefill chunk.
 """
 from __future__ import annotations
 
@@ -97,11 +99,14 @@ def paged_decode(q, k_pool, v_pool, block_tables, context_lens, *, n_kv: int,
 
 
 def paged_prefill(q, cu_q_lens, k_pool, v_pool, block_tables, context_lens, *, n_kv: int,
-                  block_size: int = BLOCK, scale: float | None = None, rows=None) -> np.ndarray:
+                  block_size: int = BLOCK, scale: float | None = None, rows=None,
+                  window: int | None = None) -> np.ndarray:
     """Causal attention of a chunk of query tokens per sequence.
 
     q [total_q, H, D]; chunk of sequence s is rows cu[s]..cu[s+1]-1; returns
-    float64 [total_q, H, D] (rows not listed in `rows` are NaN).
+    float64 [total_q, H, D] (rows not listed in `rows` are NaN). With a
+    sliding window W the row at position p attends keys max(0, p - W + 1) .. p
+    (the decode's window, read for every row of the chunk).
     """
     q = np.asarray(q, dtype=np.float64)
     T, H, D = q.shape
@@ -122,6 +127,8 @@ def paged_prefill(q, cu_q_lens, k_pool, v_pool, block_tables, context_lens, *, n
         K = gather(k_pool, block_tables[s], n, block_size)
         V = gather(v_pool, block_tables[s], n, block_size)
         visible = np.arange(n)[None, :] <= pos[:, None]  # key t visible to row iff t <= pos
+        if window is not None:
+            visible &= np.arange(n)[None, :] > pos[:, None] - int(window)  # ... and t >= pos - W + 1
         for h in range(H):
             kvh = h // G
             # one softmax_attention per row, written as one matrix product

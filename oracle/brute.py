@@ -54,14 +54,15 @@ def decode_attention(q, k_pool, v_pool, table, n_ctx, n_kv, block_size=16, windo
     return out
 
 
-def prefill_attention(qrows, k_pool, v_pool, table, n_ctx, n_kv, block_size=16):
+def prefill_attention(qrows, k_pool, v_pool, table, n_ctx, n_kv, block_size=16, window=None):
     """qrows: [q_len][H][D], the last q_len tokens of a context of n_ctx.
-    Row i attends keys 0..n_ctx-q_len+i."""
+    Row i attends keys 0..n_ctx-q_len+i (with a window W, only the last W of
+    them)."""
     q_len = len(qrows)
     out = []
     for i in range(q_len):
         pos = n_ctx - q_len + i
-        out.append(decode_attention(qrows[i], k_pool, v_pool, table, pos + 1, n_kv, block_size))
+        out.append(decode_attention(qrows[i], k_pool, v_pool, table, pos + 1, n_kv, block_size, window=window))
     return out
 
 

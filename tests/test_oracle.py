@@ -263,6 +263,52 @@ def test_prefix_retrieval_probe(dtype, shared_pos):
         np.testing.assert_allclose(out[s], np.array(ref), rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_windowed_prefill_vs_brute_force(seed):
+    """Windowed chunk rows: row at position p attends keys p - W + 1 .. p
+    (brute force, windows from one token to past the context)."""
+    g = np.random.default_rng(90 + seed)
+    n_kv, G, d = int(g.choice([1, 2])), int(g.choice([1, 2, 4])), int(g.choice([4, 8]))
+    ctx = g.integers(1, 50, size=3)
+    qlens = [int(g.integers(0, c + 1)) for c in ctx]
+    c = make_prefill_case(n_kv * G, n_kv, d, "bf16" if seed % 2 else "f32", ctx, qlens, 190 + seed)
+    q, k, v = f64(c, c.q), f64(c, c.k_slots), f64(c, c.v_slots)
+    for w in (1, 2, 15, 16, 17, 60):
+        out = oracle.paged_prefill(q, c.cu_q_lens, k, v, c.block_tables, c.context_lens, n_kv=n_kv, window=w)
+        for s in range(c.num_seqs):
+            lo, hi = int(c.cu_q_lens[s]), int(c.cu_q_lens[s + 1])
+            if hi == lo:
+                continue
+            ref = brute.prefill_attention(q[lo:hi].tolist(), k.tolist(), v.tolist(), c.block_tables[s].tolist(),
+                                          int(c.context_lens[s]), n_kv, window=w)
+            np.testing.assert_allclose(out[lo:hi], np.array(ref), rtol=0, atol=1e-12)
+
+
+def test_windowed_prefill_special_cases():
+    """W = 1: each row returns its own V exactly; W past every position: the
+    unwindowed chunk; the last row equals the windowed decode of the whole
+    context."""
+    c = make_prefill_case(8, 2, 16, "bf16", [40, 17, 100], [40, 5, 33], 195)
+    q, k, v = f64(c, c.q), f64(c, c.k_slots), f64(c, c.v_slots)
+    one = oracle.paged_prefill(q, c.cu_q_lens, k, v, c.block_tables, c.context_lens, n_kv=2, window=1)
+    for s in range(c.num_seqs):
+        lo, hi = int(c.cu_q_lens[s]), int(c.cu_q_lens[s + 1])
+        n = int(c.context_lens[s])
+        for i in range(hi - lo):
+            p = n - (hi - lo) + i
+            slot = c.block_tables[s, p // 16] * 16 + p % 16
+            for h in range(8):
+                assert np.array_equal(one[lo + i, h], v[slot, h // 4])
+    full = run_prefill(c)
+    wide = oracle.paged_prefill(q, c.cu_q_lens, k, v, c.block_tables, c.context_lens, n_kv=2, window=1000)
+    assert np.array_equal(full, wide)
+    w = 23
+    win = oracle.paged_prefill(q, c.cu_q_lens, k, v, c.block_tables, c.context_lens, n_kv=2, window=w)
+    last_rows = np.asarray(c.cu_q_lens[1:]) - 1
+    dec = oracle.paged_decode(q[last_rows], k, v, c.block_tables, c.context_lens, n_kv=2, window=w)
+    np.testing.assert_allclose(win[last_rows], dec, rtol=0, atol=1e-14)
+
+
 def test_prefill_vs_brute_force():
     c = make_prefill_case(4, 2, 8, "f32", [5, 33, 20], [5, 7, 1], 15)
     out = run_prefill(c)
