@@ -5,6 +5,7 @@
  *   paged_attn_decode         single-query attention of a batch of sequences
  *   paged_attn_decode_window  the same over each sequence's last W tokens
  *   paged_attn_prefill_chunk  causal attention of a chunk of prompt tokens
+ *   paged_attn_prefill_chunk_window  the same over each row's last W tokens
  *   kv_quantize               symmetric int8 / int4 codes + fp16 scales
  *   paged_kv_write            scatter new tokens' K/V into their cache slots
  * plus a few host-only helpers (sizes, error strings).
@@ -64,7 +65,7 @@
  *    8  int8 code  + fp16 scale per (block, KV head) (requires PA_BF16)
  *    4  int4 code  + fp16 scale per (block, KV head) (requires PA_BF16)
  *   PA_KV_FP8  OCP fp8 e4m3 code + fp16 scale per (block, KV head)
- *              (requires PA_BF16; decode only). One byte per element, laid
+ *              (requires PA_BF16). One byte per element, laid
  *              out as int8; bit 7 sign, bits 6..3 exponent (bias 7), bits
  *              2..0 mantissa, exponent 0 subnormal, 0x7F / 0xFF NaN.
  * A pool is an array of tiles, one per (block b, KV head h), each holding the
@@ -269,8 +270,9 @@ int paged_attn_decode_window(const void* q, const void* k_pool, const void* v_po
  * cu_q_lens     int32 [num_seqs + 1] device prefix sums, cu_q_lens[0] = 0,
  *               cu_q_lens[num_seqs] = total_q, 0 <= q_len_s <= max_q_len,
  *               q_len_s <= context_lens[s]
- * other arguments as for paged_attn_decode, except that fp8 pools
- * (PA_KV_FP8) give PA_ERR_UNSUPPORTED. No workspace.
+ * other arguments as for paged_attn_decode (every pool format, fp8
+ * included). No workspace: each chunk row is computed whole by one
+ * workgroup.
  * ------------------------------------------------------------------------ */
 int paged_attn_prefill_chunk(const void* q, const int32_t* cu_q_lens, int total_q, int max_q_len,
                              const void* k_pool, const void* v_pool,
@@ -280,6 +282,24 @@ int paged_attn_prefill_chunk(const void* q, const int32_t* cu_q_lens, int total_
                              int num_seqs, int num_blocks, int block_size,
                              int n_heads, int n_kv_heads, int d_head, int dtype, int kv_bits,
                              void* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Sliding-window causal prefill of a chunk ([IR] "The memory equation":
+ * sliding-window attention; [TAI] "The KV cache": sliding-window layers). As
+ * paged_attn_prefill_chunk, but the row at absolute position p attends only
+ * keys max(0, p - window_tokens + 1) .. p, the decode window's rule applied
+ * to every row; window_tokens >= 1 (else PA_ERR_INVALID_ARG), and a window
+ * reaching back past key 0 is the full causal prefill. Blocks wholly before
+ * every row's window are not read.
+ * ------------------------------------------------------------------------ */
+int paged_attn_prefill_chunk_window(const void* q, const int32_t* cu_q_lens, int total_q, int max_q_len,
+                                    const void* k_pool, const void* v_pool,
+                                    const uint16_t* k_scales, const uint16_t* v_scales,
+                                    const int32_t* block_tables, int max_blocks_per_seq,
+                                    const int32_t* context_lens, int max_context_len,
+                                    int num_seqs, int num_blocks, int block_size,
+                                    int n_heads, int n_kv_heads, int d_head, int dtype, int kv_bits,
+                                    void* out, int window_tokens, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Symmetric b-bit quantization of a bf16 pool ([JE] "KV-cache quantization":

@@ -25,7 +25,7 @@ BLOCK_SIZE = 16
 EXPORTS = (
     "pa_error_string", "pa_tile_bytes", "pa_kv_bytes_per_token", "pa_kv_cache_bytes",
     "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_decode_window", "paged_attn_prefill_chunk",
-    "paged_attn_decode_noalloc",
+    "paged_attn_decode_noalloc", "paged_attn_prefill_chunk_window",
     "kv_quantize", "paged_kv_write", "pa_copy_blocks", "pa_hbm_read_probe", "pa_take_block_id_error",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_ref_count", "pa_bm_add", "pa_bm_append",
     "pa_bm_fork", "pa_bm_release", "pa_bm_num_tokens", "pa_bm_table",
@@ -63,6 +63,9 @@ def _declare(lib):
     lib.paged_attn_prefill_chunk.restype = i
     lib.paged_attn_prefill_chunk.argtypes = [vp, vp, i, i, vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, i, i, i,
                                              vp, vp]
+    lib.paged_attn_prefill_chunk_window.restype = i
+    lib.paged_attn_prefill_chunk_window.argtypes = [vp, vp, i, i, vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, i,
+                                                    i, i, vp, i, vp]
     lib.kv_quantize.restype = i
     lib.kv_quantize.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
     lib.paged_kv_write.restype = i
@@ -249,8 +252,9 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, *, n_kv_heads, max_con
 
 
 def prefill_chunk(q, cu_q_lens, k_pool, v_pool, block_tables, context_lens, *, n_kv_heads, max_q_len,
-                  max_context_len, kv_bits=None, k_scales=None, v_scales=None, out=None, stream=None):
-    """paged_attn_prefill_chunk. q [total_q, H, D]; cu_q_lens [S+1] int32."""
+                  max_context_len, kv_bits=None, k_scales=None, v_scales=None, out=None, stream=None, window=None):
+    """paged_attn_prefill_chunk, or paged_attn_prefill_chunk_window when a
+    window (tokens, >= 1) is given. q [total_q, H, D]; cu_q_lens [S+1] int32."""
     dev = _gpu(q, cu_q_lens, k_pool, v_pool, block_tables, context_lens, k_scales, v_scales, out)
     T, H, D = q.shape
     dt = _dtype_code(q.dtype)
@@ -260,11 +264,14 @@ def prefill_chunk(q, cu_q_lens, k_pool, v_pool, block_tables, context_lens, *, n
     if out is None:
         out = torch.empty_like(q)
     S = context_lens.shape[0]
-    st = lib().paged_attn_prefill_chunk(
-        _p(q), _p(cu_q_lens), T, int(max_q_len), _p(k_pool), _p(v_pool), _p(k_scales), _p(v_scales),
-        _p(block_tables), block_tables.shape[1], _p(context_lens), int(max_context_len), S, nb, BLOCK_SIZE,
-        H, n_kv_heads, D, dt, kv_bits, _p(out), _stream(stream, dev))
-    _check("paged_attn_prefill_chunk", st)
+    args = (_p(q), _p(cu_q_lens), T, int(max_q_len), _p(k_pool), _p(v_pool), _p(k_scales), _p(v_scales),
+            _p(block_tables), block_tables.shape[1], _p(context_lens), int(max_context_len), S, nb, BLOCK_SIZE,
+            H, n_kv_heads, D, dt, kv_bits, _p(out))
+    if window is None:
+        _check("paged_attn_prefill_chunk", lib().paged_attn_prefill_chunk(*args, _stream(stream, dev)))
+    else:
+        _check("paged_attn_prefill_chunk_window",
+               lib().paged_attn_prefill_chunk_window(*args, int(window), _stream(stream, dev)))
     return out
 
 

@@ -309,20 +309,23 @@ int paged_attn_decode_window(const void* q, const void* k_pool, const void* v_po
                        out, workspace, workspace_bytes, partition_blocks, window_tokens, stream);
 }
 
-int paged_attn_prefill_chunk(const void* q, const int32_t* cu_q_lens, int total_q, int max_q_len,
-                             const void* k_pool, const void* v_pool,
-                             const uint16_t* k_scales, const uint16_t* v_scales,
-                             const int32_t* block_tables, int max_blocks_per_seq,
-                             const int32_t* context_lens, int max_context_len,
-                             int num_seqs, int num_blocks, int block_size,
-                             int n_heads, int n_kv_heads, int d_head, int dtype, int kv_bits,
-                             void* out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both prefill entry points; window 0 = none.
+int prefill_impl(const void* q, const int32_t* cu_q_lens, int total_q, int max_q_len, const void* k_pool,
+                 const void* v_pool, const uint16_t* k_scales, const uint16_t* v_scales, const int32_t* block_tables,
+                 int max_blocks_per_seq, const int32_t* context_lens, int max_context_len, int num_seqs,
+                 int num_blocks, int block_size, int n_heads, int n_kv_heads, int d_head, int dtype, int kv_bits,
+                 void* out, int window, void* stream) {
+    if (window < 0) return PA_ERR_INVALID_ARG;
     if (!valid_common(num_seqs, num_blocks, block_size, n_heads, n_kv_heads, d_head)) return PA_ERR_INVALID_ARG;
     if (max_blocks_per_seq <= 0 || max_context_len < 0 || total_q < 0 || max_q_len < 0) return PA_ERR_INVALID_ARG;
     if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID_ARG;
     if (!valid_kv_bits(kv_bits)) return PA_ERR_INVALID_ARG;
     const int fmt = fmt_of(dtype, kv_bits);
-    if (fmt < 0 || kv_bits == PA_KV_FP8) return PA_ERR_UNSUPPORTED;
+    if (fmt < 0) return PA_ERR_UNSUPPORTED;
     if (d_head != 64 && d_head != 128) return PA_ERR_UNSUPPORTED;
     const int G = n_heads / n_kv_heads;
     if (G > PA_MAX_GROUP) return PA_ERR_UNSUPPORTED;
@@ -349,9 +352,41 @@ int paged_attn_prefill_chunk(const void* q, const int32_t* cu_q_lens, int total_
     p.group = G;
     p.max_q_len = max_q_len;
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d_head));
+    p.window = window;
     const hipError_t e = pa::launch_prefill(p, d_head, fmt, static_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_prefill_chunk(const void* q, const int32_t* cu_q_lens, int total_q, int max_q_len,
+                             const void* k_pool, const void* v_pool,
+                             const uint16_t* k_scales, const uint16_t* v_scales,
+                             const int32_t* block_tables, int max_blocks_per_seq,
+                             const int32_t* context_lens, int max_context_len,
+                             int num_seqs, int num_blocks, int block_size,
+                             int n_heads, int n_kv_heads, int d_head, int dtype, int kv_bits,
+                             void* out, void* stream) {
+    return prefill_impl(q, cu_q_lens, total_q, max_q_len, k_pool, v_pool, k_scales, v_scales, block_tables,
+                        max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_blocks, block_size, n_heads,
+                        n_kv_heads, d_head, dtype, kv_bits, out, 0, stream);
+}
+
+int paged_attn_prefill_chunk_window(const void* q, const int32_t* cu_q_lens, int total_q, int max_q_len,
+                                    const void* k_pool, const void* v_pool,
+                                    const uint16_t* k_scales, const uint16_t* v_scales,
+                                    const int32_t* block_tables, int max_blocks_per_seq,
+                                    const int32_t* context_lens, int max_context_len,
+                                    int num_seqs, int num_blocks, int block_size,
+                                    int n_heads, int n_kv_heads, int d_head, int dtype, int kv_bits,
+                                    void* out, int window_tokens, void* stream) {
+    if (window_tokens <= 0) return PA_ERR_INVALID_ARG;
+    return prefill_impl(q, cu_q_lens, total_q, max_q_len, k_pool, v_pool, k_scales, v_scales, block_tables,
+                        max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_blocks, block_size, n_heads,
+                        n_kv_heads, d_head, dtype, kv_bits, out, window_tokens, stream);
 }
 
 int kv_quantize(const void* src, void* codes, uint16_t* scales, const int32_t* block_ids, int n_ids,

@@ -128,6 +128,7 @@ struct PrefillParams {
     int group;
     int max_q_len;
     float scale_log2;
+    int window;         // sliding window in tokens (0: none): row at position p attends keys p - window + 1 .. p
     // prefix pass only (see kPrefixRows)
     float* part_acc;
     float* part_ml;

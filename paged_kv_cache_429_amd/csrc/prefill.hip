@@ -61,9 +61,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p, int 
 
     const int i_last = min(qlen, i0 + QT) - 1;
     const int kend = shift + i_last + 1;  // keys [0, kend) are visible to some row
+    // with a sliding window, keys before kbeg are visible to no row
+    const int kbeg = p.window > 0 ? max(0, shift + i0 - p.window + 1) : 0;
 
-    // per column group: row, causal limit, Q operand
-    int pos[C];
+    // per column group: row, causal limit (and window start), Q operand
+    int pos[C], plo[C];
     bool store_row[C];
     u32x4 qop[C][M::KSTEPS];
     const uint16_t* qbase = reinterpret_cast<const uint16_t*>(p.q);
@@ -75,6 +77,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p, int 
         store_row[cg] = row_ok;
         const bool live = row_ok && ps >= 0;
         pos[cg] = live ? ps : kend - 1;  // dead columns see every key (their Q is 0) and are not stored
+        plo[cg] = live && p.window > 0 ? ps - p.window + 1 : -1;
 #pragma unroll
         for (int kk = 0; kk < M::KSTEPS; ++kk) {
             if (live) {
@@ -87,8 +90,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p, int 
     }
     const int wave_first_row = i0 + wave * C * TPG;
     const int wave_last_row = min(qlen - 1, i0 + (wave * C + C) * TPG - 1);
-    // last key any row of this wave sees (-1: the wave has no rows)
+    // last key any row of this wave sees (-1: the wave has no rows), and the
+    // first (the window's start of its first row)
     const int wave_kmax = wave_first_row < qlen ? shift + wave_last_row : -1;
+    const int wave_kmin = p.window > 0 ? shift + wave_first_row - p.window + 1 : 0;
 
     float m[C], l[C];
     f32x4 acc[C][M::NB];
@@ -107,12 +112,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p, int 
     const int npairs = (nblk + 1) >> 1;
 
     int my_id = 0;
-    int window = -1;
+    int idwin = -1;
     u32x4 pre[PER_T];
     auto fetch = [&](int k) {
-        if (((2 * k) >> 6) != window) {
-            window = (2 * k) >> 6;
-            my_id = load_ids(p.tables, trow, window << 6, min(64, nblk - (window << 6)), p.num_blocks);
+        if (((2 * k) >> 6) != idwin) {
+            idwin = (2 * k) >> 6;
+            my_id = load_ids(p.tables, trow, idwin << 6, min(64, nblk - (idwin << 6)), p.num_blocks);
         }
         const int j0 = (2 * k) & 63;
         const int id0 = readlane(my_id, j0);
@@ -130,8 +135,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p, int 
         }
     };
 
-    if (npairs > 0) fetch(0);
-    for (int k = 0; k < npairs; ++k) {
+    const int k0 = kbeg / (2 * kBlock);  // first pair any row sees
+    if (npairs > k0) fetch(k0);
+    for (int k = k0; k < npairs; ++k) {
         const int j0 = (2 * k) & 63;
         const int id0 = readlane(my_id, j0);
         const bool has1 = 2 * k + 1 < nblk;
@@ -147,6 +153,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p, int 
 
         const int key0 = 32 * k;
         if (key0 > wave_kmax) continue;  // every row of this wave is before this pair
+        if (key0 + 31 < wave_kmin) continue;  // ... or past this pair's window
 
         float ks0 = 1.f, ks1 = 1.f, vs0 = 1.f, vs1 = 1.f;
         if (is_quant<FMT>()) {
@@ -176,8 +183,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p, int 
             float x[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                x[i] = (tok0 + i <= pos[cg]) ? s0[i] * c0 : kNegInf;
-                x[4 + i] = (has1 && tok1 + i <= pos[cg]) ? s1[i] * c1 : kNegInf;
+                x[i] = (tok0 + i <= pos[cg] && tok0 + i >= plo[cg]) ? s0[i] * c0 : kNegInf;
+                x[4 + i] = (has1 && tok1 + i <= pos[cg] && tok1 + i >= plo[cg]) ? s1[i] * c1 : kNegInf;
             }
             float mx = x[0];
 #pragma unroll
@@ -185,14 +192,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p, int 
             mx = wave_max_xor(mx, 16);
             mx = wave_max_xor(mx, 32);
             const float mnew = fmaxf(m[cg], mx);
-            // mnew is finite: key 0 is visible to every column, and pairs are in order
-            const float alpha = __builtin_amdgcn_exp2f(m[cg] - mnew);
+            // without a window mnew is finite (key 0 is visible to every
+            // column, and pairs are in order); with one, a column whose window
+            // starts past this pair has seen no key yet and its state stays 0
+            const float mref = (mnew == kNegInf) ? 0.f : mnew;
+            const float alpha = __builtin_amdgcn_exp2f(m[cg] - mref);
             m[cg] = mnew;
             float pr[8];
             float psum = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                pr[i] = __builtin_amdgcn_exp2f(x[i] - mnew);
+                pr[i] = __builtin_amdgcn_exp2f(x[i] - mref);
                 psum += pr[i];
             }
             l[cg] = l[cg] * alpha + psum;
@@ -387,6 +397,9 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
     }
     const int wfirst = i0 + wave * TPW;
     int wave_kmax = 0, nblk, nstage;
+    // with a sliding window: the first key any row of the workgroup sees, and
+    // the window starts of the wave's first and last rows
+    int wave_klo = 0, wave_khi = 0;
     if constexpr (PREFIX) {
         nblk = st_end * kStageBlocks;
         nstage = st_end;
@@ -397,7 +410,13 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
         nblk = (kend + kBlock - 1) / kBlock;
         nstage = (kend + kStageKeys - 1) / kStageKeys;
         st_end = nstage;
+        if (p.window > 0) {
+            st_begin = max(0, shift + i0 - p.window + 1) / kStageKeys;
+            wave_klo = shift + wfirst - p.window + 1;
+            wave_khi = shift + min(qlen - 1, wfirst + TPW - 1) - p.window + 1;
+        }
     }
+    const int plo = p.window > 0 ? pos - p.window + 1 : -1;  // the row's first visible key
 
     const int32_t* trow = p.tables + (size_t)s * p.max_blocks;
     const uint8_t* kpool = reinterpret_cast<const uint8_t*>(p.k_pool);
@@ -508,9 +527,9 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float x = sc[kt][r] * p.scale_log2;
-                if (DIAG) {
+                if (DIAG) {  // causal diagonal, or a window's start, inside the stage
                     const int key = kb + 32 * kt + 8 * (r / 4) + 4 * half + r % 4;
-                    x = key <= pos ? x : kNegInf;
+                    x = key <= pos && key >= plo ? x : kNegInf;
                 }
                 sc[kt][r] = x;
                 mx = fmaxf(mx, x);
@@ -573,11 +592,13 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
         if (st + 1 < nstage) prefetch(st + 1, nbuf);
         const int kb = st * kStageKeys;
         // Rows of this wave whose position is at least kb + 63 see the whole
-        // stage; only a stage on the causal diagonal needs the mask. (Rows
-        // past the chunk end never get stored.)
-        if (PREFIX || kb + kStageKeys - 1 <= shift + wfirst) {
+        // stage; only a stage on the causal diagonal needs the mask, or, with
+        // a window, one holding some row's window start. A stage past every
+        // row, or wholly before every row's window, is skipped. (Rows past the
+        // chunk end never get stored.)
+        if (PREFIX || (kb + kStageKeys - 1 <= shift + wfirst && kb >= wave_khi)) {
             stage(buf, kb, std::false_type{});
-        } else if (kb <= wave_kmax) {
+        } else if (kb <= wave_kmax && kb + kStageKeys - 1 >= wave_klo) {
             stage(buf, kb, std::true_type{});
         }
         if (st + 1 < nstage) {
@@ -655,8 +676,8 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(PrefillParams pp)
     u.kvh = kvh;
     u.part = 0;
     u.slot0 = 0;
-    u.lo = 0;
     u.ctx = pos + 1;
+    u.lo = pp.window > 0 ? max(0, pos - pp.window + 1) : 0;
     if (u.ctx <= 0) {
         for (int idx = threadIdx.x; idx < p.group * D; idx += kThreads)
             store_out<D, true>(p, ((size_t)u.s * p.n_heads + kvh * p.group) * D + idx, 0.f);
@@ -664,7 +685,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(PrefillParams pp)
     }
     u.nblk = (u.ctx + kBlock - 1) / kBlock;
     u.nparts = 1;
-    u.b_begin = 0;
+    u.b_begin = u.lo / kBlock;  // blocks wholly before the window are not read
     u.b_end = u.nblk;
     const float* qg = reinterpret_cast<const float*>(p.q) + ((size_t)u.s * p.n_heads + kvh * p.group) * D;
     for (int idx = threadIdx.x; idx < p.group * D; idx += kThreads) qs[idx] = qg[idx];
@@ -732,6 +753,7 @@ hipError_t launch_prefill(const PrefillParams& p, int d, int fmt, hipStream_t st
                 return launch_mfma<128, FMT_BF16, C>(p, stream);
             case FMT_I8: return launch_mfma<128, FMT_I8, C>(p, stream);
             case FMT_I4: return launch_mfma<128, FMT_I4, C>(p, stream);
+            case FMT_F8: return launch_mfma<128, FMT_F8, C>(p, stream);
         }
     } else if (d == 64) {
         switch (fmt) {
@@ -739,6 +761,7 @@ hipError_t launch_prefill(const PrefillParams& p, int d, int fmt, hipStream_t st
             case FMT_BF16: return launch_mfma<64, FMT_BF16, C>(p, stream);
             case FMT_I8: return launch_mfma<64, FMT_I8, C>(p, stream);
             case FMT_I4: return launch_mfma<64, FMT_I4, C>(p, stream);
+            case FMT_F8: return launch_mfma<64, FMT_F8, C>(p, stream);
         }
     }
     return hipErrorInvalidValue;

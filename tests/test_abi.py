@@ -149,8 +149,11 @@ def test_other_entry_points_reject_on_host(B):
     bad[0] = None
     assert L.paged_attn_prefill_chunk(*bad) == -1
     bad = list(args)
-    bad[19], bad[6], bad[7] = 264, one, one  # fp8 pools: decode only
+    bad[18], bad[19], bad[6], bad[7] = 0, 264, one, one  # fp8 pools need bf16 queries
     assert L.paged_attn_prefill_chunk(*bad) == -2
+    # the windowed prefill: window >= 1
+    assert L.paged_attn_prefill_chunk_window(*args[:-1], 0, None) == -1
+    assert L.paged_attn_prefill_chunk_window(*args[:-1], -5, None) == -1
     assert L.kv_quantize(one, one, one, one, 0, 4, 2, 16, 128, 264, 0, None) == 0   # fp8 accepted
 
 

@@ -132,32 +132,17 @@ def test_fp8_retrieval_probe_all_codes_exact(lib, pb, d):
     assert len(seen) >= 200
 
 
-def test_workload4_fp8_sampled(lib):
-    """The whole 128 x 8000 batch in the benchmark's launch configuration,
-    checked on sampled sequences (the oracle quantizes only their blocks)."""
-    c = make_config_case(4)
-    kc, vc, ks, vs = _fp8_case(c)
-    got = dev_to_f64(gpu_decode(c, kp=kc, vp=vc, kv_bits=FP8, k_scales=ks, v_scales=vs))
-    seqs = [0, 5, 77, 127]
-    used = np.unique(c.block_tables[seqs].ravel())
-    used = used[used >= 0]
-    rows = (used[:, None] * 16 + np.arange(16)[None, :]).ravel()
-    kq, kqs = oracle.quantize_tiles_fp8(bf16_bits_to_f32(c.k_slots[rows]))
-    vq, vqs = oracle.quantize_tiles_fp8(bf16_bits_to_f32(c.v_slots[rows]))
-    kd = np.zeros(c.k_slots.shape, dtype=np.float64)
-    vd = np.zeros(c.v_slots.shape, dtype=np.float64)
-    kd[rows] = oracle.dequantize_fp8(kq, kqs)
-    vd[rows] = oracle.dequantize_fp8(vq, vqs)
-    ref = oracle_decode(c, seqs=seqs, k_slots=kd, v_slots=vd)
-    assert_close(got[seqs], ref[seqs], "bf16", "workload4 fp8")
-
-
-def test_fp8_prefill_unsupported(lib):
-    c = make_decode_case(8, 2, 128, "bf16", [40], 9040, pool_factor=1.2)
+def test_fp8_prefill_matches_decode(lib):
+    """fp8 pools in the prefill: a one-token chunk per sequence equals the
+    decode of the same query on the same codes (the whole 128 x 8000 batch is
+    checked against the oracle in test_kvops_gpu.py; chunk parity in
+    test_prefill_gpu.py)."""
+    c = make_decode_case(8, 2, 128, "bf16", [40, 333, 17], 9040, pool_factor=1.2)
     kc, vc, ks, vs = _fp8_case(c)
     tables, ctx = upload_meta(c)
     q = np_to_dev(c.q, "bf16")
-    cu = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
-    with pytest.raises(B.PagedAttnError):
-        B.prefill_chunk(q, cu, kc, vc, tables, ctx, n_kv_heads=2, max_q_len=1, max_context_len=40, kv_bits=FP8,
-                        k_scales=ks, v_scales=vs)
+    cu = torch.arange(c.num_seqs + 1, dtype=torch.int32, device="cuda")
+    pre = B.prefill_chunk(q, cu, kc, vc, tables, ctx, n_kv_heads=2, max_q_len=1, max_context_len=333, kv_bits=FP8,
+                          k_scales=ks, v_scales=vs)
+    dec = gpu_decode(c, kp=kc, vp=vc, kv_bits=FP8, k_scales=ks, v_scales=vs)
+    assert_close(dev_to_f64(pre), dev_to_f64(dec), "bf16", "fp8 q_len 1 vs decode")

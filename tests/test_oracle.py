@@ -309,6 +309,26 @@ def test_windowed_prefill_special_cases():
     np.testing.assert_allclose(win[last_rows], dec, rtol=0, atol=1e-14)
 
 
+@pytest.mark.parametrize("window", [1, 5, 64, 65, 300])
+def test_windowed_prefill_first_key_probe(window):
+    """The causal probe with its queries negated: scores fall strictly with
+    position, so each windowed row returns V at max(0, p - W + 1), the first
+    key its window shows (float64 weights of the others below 1e-60)."""
+    c = make_prefill_probe_case(8, 2, 128, "f32", [300, 64, 17], [100, 64, 3], 196)
+    c.q = -c.q
+    out = oracle.paged_prefill(f64(c, c.q), c.cu_q_lens, f64(c, c.k_slots), f64(c, c.v_slots), c.block_tables,
+                               c.context_lens, n_kv=2, window=window)
+    v = f64(c, c.v_slots)
+    for s in range(c.num_seqs):
+        lo, hi = int(c.cu_q_lens[s]), int(c.cu_q_lens[s + 1])
+        n = int(c.context_lens[s])
+        for i in range(hi - lo):
+            p = max(0, n - (hi - lo) + i - window + 1)
+            sl = c.block_tables[s, p // 16] * 16 + p % 16
+            for h in range(8):
+                np.testing.assert_allclose(out[lo + i, h], v[sl, h // 4], rtol=0, atol=1e-40)
+
+
 def test_prefill_vs_brute_force():
     c = make_prefill_case(4, 2, 8, "f32", [5, 33, 20], [5, 7, 1], 15)
     out = run_prefill(c)

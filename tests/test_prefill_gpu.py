@@ -13,7 +13,7 @@ from tests.layout_ref import pack_pool
 pytestmark = pytest.mark.gpu
 
 
-def gpu_prefill(c, kp=None, vp=None, kv_bits=None, k_scales=None, v_scales=None):
+def gpu_prefill(c, kp=None, vp=None, kv_bits=None, k_scales=None, v_scales=None, window=None):
     if kp is None:
         kp, vp = upload_pools(c)
     q = np_to_dev(c.q, c.dtype)
@@ -22,16 +22,16 @@ def gpu_prefill(c, kp=None, vp=None, kv_bits=None, k_scales=None, v_scales=None)
     ctx = torch.from_numpy(c.context_lens.astype(np.int32)).cuda()
     out = B.prefill_chunk(q, cu, kp, vp, tables, ctx, n_kv_heads=c.n_kv, max_q_len=max(1, c.max_q_len),
                           max_context_len=max(1, c.max_context_len), kv_bits=kv_bits, k_scales=k_scales,
-                          v_scales=v_scales)
+                          v_scales=v_scales, window=window)
     torch.cuda.synchronize()
     return out
 
 
-def oracle_prefill(c, rows=None, k=None, v=None):
+def oracle_prefill(c, rows=None, k=None, v=None, window=None):
     k = oracle.as_f64(c.k_slots, c.dtype) if k is None else k
     v = oracle.as_f64(c.v_slots, c.dtype) if v is None else v
     return oracle.paged_prefill(oracle.as_f64(c.q, c.dtype), c.cu_q_lens, k, v, c.block_tables, c.context_lens,
-                                n_kv=c.n_kv, rows=rows)
+                                n_kv=c.n_kv, rows=rows, window=window)
 
 
 @pytest.mark.parametrize("n_heads,n_kv,d,dtype", [
@@ -62,17 +62,76 @@ def test_prefill_causal_probe_exact(lib, dtype):
                 assert np.array_equal(got[lo + i, h], v[sl, h // 4]), (s, i, h)
 
 
-@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("bits", [8, 4, 264])  # 264: fp8 (e4m3)
 def test_prefill_quantized(lib, bits):
     c = make_prefill_case(32, 8, 128, "bf16", [700, 90], [300, 90], 502 + bits)
     kp, vp = upload_pools(c)
     kc, ks = B.quantize(kp, bits=bits, kind=0, n_kv_heads=8, d_head=128)
     vc, vs = B.quantize(vp, bits=bits, kind=1, n_kv_heads=8, d_head=128)
     got = dev_to_f64(gpu_prefill(c, kp=kc, vp=vc, kv_bits=bits, k_scales=ks, v_scales=vs))
-    rk, rks = oracle.quantize_tiles(bf16_bits_to_f32(c.k_slots), bits)
-    rv, rvs = oracle.quantize_tiles(bf16_bits_to_f32(c.v_slots), bits)
-    ref = oracle_prefill(c, k=oracle.dequantize(rk, rks), v=oracle.dequantize(rv, rvs))
-    assert_close(got, ref, "bf16", f"prefill int{bits}")
+    ref = oracle_prefill(c, k=_dequantized(c.k_slots, bits), v=_dequantized(c.v_slots, bits))
+    assert_close(got, ref, "bf16", f"prefill kv_bits {bits}")
+
+
+def _dequantized(slots, bits):
+    x = bf16_bits_to_f32(slots)
+    if bits == B.PA_KV_FP8:
+        return oracle.dequantize_fp8(*oracle.quantize_tiles_fp8(x))
+    return oracle.dequantize(*oracle.quantize_tiles(x, bits))
+
+
+WIN_CTX = [300, 64, 17, 1, 1000, 129, 700, 2100]
+WIN_Q = [100, 64, 3, 1, 250, 0, 700, 300]
+
+
+@pytest.mark.parametrize("n_heads,n_kv,d,dtype,window", [
+    (32, 8, 128, "bf16", 1), (32, 8, 128, "bf16", 17), (32, 8, 128, "bf16", 64), (32, 8, 128, "bf16", 100),
+    (32, 8, 128, "bf16", 333), (64, 8, 128, "bf16", 65), (12, 4, 128, "bf16", 50), (16, 1, 64, "bf16", 77),
+    (8, 2, 64, "f32", 33), (8, 8, 128, "f32", 200), (32, 8, 128, "bf16", 5000),
+])
+def test_prefill_window(lib, n_heads, n_kv, d, dtype, window):
+    """Windowed chunk rows (the 32-row MFMA tile path at G dividing 32, the
+    16-column path at G = 3 and d 64, fp32), windows from one token to past
+    every context."""
+    c = make_prefill_case(n_heads, n_kv, d, dtype, WIN_CTX, WIN_Q, 520 + window + n_heads + d)
+    got = dev_to_f64(gpu_prefill(c, window=window))
+    assert_close(got, oracle_prefill(c, window=window), dtype, f"window {window}")
+
+
+@pytest.mark.parametrize("bits,window", [(8, 40), (4, 300), (264, 129)])  # 264: fp8 (e4m3)
+def test_prefill_window_quantized(lib, bits, window):
+    c = make_prefill_case(32, 8, 128, "bf16", WIN_CTX, WIN_Q, 540 + bits % 256)
+    kp, vp = upload_pools(c)
+    kc, ks = B.quantize(kp, bits=bits, kind=0, n_kv_heads=8, d_head=128)
+    vc, vs = B.quantize(vp, bits=bits, kind=1, n_kv_heads=8, d_head=128)
+    got = dev_to_f64(gpu_prefill(c, kp=kc, vp=vc, kv_bits=bits, k_scales=ks, v_scales=vs, window=window))
+    ref = oracle_prefill(c, k=_dequantized(c.k_slots, bits), v=_dequantized(c.v_slots, bits), window=window)
+    assert_close(got, ref, "bf16", f"kv_bits {bits} window {window}")
+
+
+@pytest.mark.parametrize("n_heads,n_kv,dtype", [(8, 2, "bf16"), (12, 4, "bf16"), (8, 2, "f32")])
+@pytest.mark.parametrize("window", [1, 2, 63, 64, 65, 130, 1000, 5000])
+def test_prefill_window_first_key_probe_exact(lib, n_heads, n_kv, dtype, window):
+    """The causal probe with its queries negated: scores now fall strictly
+    with position (gaps of 2**11 / sqrt(d) >= 181), so each row puts all its
+    weight on the first key its window shows, max(0, p - W + 1), and must
+    return V there exactly: this pins the window's lower edge."""
+    c = make_prefill_probe_case(n_heads, n_kv, 128, dtype, [300, 64, 17, 2100], [100, 64, 3, 700], 560 + window)
+    if dtype == "bf16":
+        c.q = c.q ^ np.uint16(0x8000)
+    else:
+        c.q = -c.q
+    got = gpu_prefill(c, window=window).float().cpu().numpy()
+    v = oracle.as_f64(c.v_slots, dtype)
+    G = n_heads // n_kv
+    for s in range(c.num_seqs):
+        lo, hi = int(c.cu_q_lens[s]), int(c.cu_q_lens[s + 1])
+        n = int(c.context_lens[s])
+        for i in range(hi - lo):
+            p = max(0, n - (hi - lo) + i - window + 1)
+            sl = c.block_tables[s, p // 16] * 16 + p % 16
+            for h in range(n_heads):
+                assert np.array_equal(got[lo + i, h], v[sl, h // G]), (s, i, h, window)
 
 
 def test_prefill_q1_matches_decode(lib):
