@@ -29,6 +29,9 @@ Pinning status (what each function is checked against lives in tests/):
                            nearest search over all codes, ties, saturation,
                            invariants of the quantized tiles.
   formulas.*               pinned: the pages' printed worked values.
+  cache_write.*            pinned: pure-Python brute force of the slot rule,
+                           appends in steps == one append, the brute-force
+                           quantizer on zero-filled partly written tiles.
   The softmax scale 1/sqrt(d_head) is a reading (the pages lose the formula);
   it is fixed by convention, not by a printed value.
 """
@@ -37,4 +40,5 @@ from .quantize import quantize_tiles, dequantize, QMAX  # noqa: F401
 from .quantize import (E4M3_MAX, e4m3_value, e4m3_round, quantize_tiles_fp8,  # noqa: F401
                        dequantize_fp8)
 from . import formulas  # noqa: F401
+from . import cache_write  # noqa: F401
 from . import brute  # noqa: F401
