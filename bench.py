@@ -1,6 +1,7 @@
 """Benchmark: paged decode attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|3|4a|4b|4f|5d|5p|5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2|3|4a|4b|4f|5d|5p|5|append]
+                    [--kv-bits 16|8|4|264] [--no-cpu-baseline]
 
 A step is one paged_attn_decode call (all G query heads of every KV head,
 every sequence of the batch, split-context merge included) over one layer's
@@ -68,6 +69,8 @@ def parse():
     ap.add_argument("--no-read-probe", action="store_true",
                     help="skip measuring the device's read ceiling (random 4 KiB tiles and a stream)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--kv-bits", type=int, default=16,
+                    help="pool format of the append workload: 16 (bf16), 8, 4 or 264 (fp8 e4m3)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device copy of this many MiB (calibrates "
                          "the HBM byte counters) and print its size and time")
@@ -378,6 +381,95 @@ def prefill_main(a, torch, B, CONFIGS):
     print(json.dumps(res), flush=True)
 
 
+def append_main(a, torch, B, CONFIGS):
+    """Workload 'append': paged_kv_append writing every token of the
+    Llama-3-8B-shaped layer's 64 sequences (contexts U[512, 4096]) into an
+    empty pool in one call, as a prompt prefill would, through the block
+    table; for quantized pools (--kv-bits 8, 4, 264) the blocks are quantized
+    on write. Algorithmic bytes: the new K and V rows read, the pool bytes of
+    their tokens written, and for quantized pools the scales written and the
+    staging tiles of the partly filled last blocks written. One decode
+    step's append (one token per sequence, rewriting each sequence's last
+    position; timing only) is timed beside it."""
+    from synth import make_config_case
+    c = make_config_case(2)
+    bits = a.kv_bits
+    quant = bits in (8, 4, PA_KV_FP8)
+    S, nkv, d = c.num_seqs, c.n_kv, c.d
+    ctx = c.context_lens.astype(np.int64)
+    tokens = int(ctx.sum())
+    g = torch.Generator(device="cuda").manual_seed(4292)
+    kn = torch.randn((tokens, nkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    vn = torch.randn((tokens, nkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    kp = B.alloc_pool(c.num_blocks, nkv, d, bits)
+    vp = B.alloc_pool(c.num_blocks, nkv, d, bits)
+    ks = vs = kst = vst = None
+    if quant:
+        ks, vs = B.alloc_scales(c.num_blocks, nkv), B.alloc_scales(c.num_blocks, nkv)
+        kst = torch.zeros((S, nkv, 16, d), dtype=torch.bfloat16, device="cuda")
+        vst = torch.zeros_like(kst)
+    tables = torch.from_numpy(np.ascontiguousarray(c.block_tables)).cuda()
+    lens = torch.from_numpy(ctx.astype(np.int32)).cuda()
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)).cuda()
+    cu1 = torch.arange(S + 1, dtype=torch.int32, device="cuda")
+    k1, v1 = kn[:S].contiguous(), vn[:S].contiguous()
+
+    def fill():
+        B.kv_append(kn, vn, cu, tables, lens, kp, vp, n_kv_heads=nkv, max_new=int(ctx.max()), kv_bits=bits,
+                    k_scales=ks, v_scales=vs, k_stage=kst, v_stage=vst)
+
+    def one_token():
+        B.kv_append(k1, v1, cu1, tables, lens, kp, vp, n_kv_heads=nkv, max_new=1, kv_bits=bits,
+                    k_scales=ks, v_scales=vs, k_stage=kst, v_stage=vst)
+
+    def timed(fn, n):
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        for i in range(n):
+            ev[i][0].record(stream)
+            fn()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([x.elapsed_time(y) for x, y in ev])
+
+    for _ in range(a.warmup):
+        fill()
+        one_token()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        fill()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = timed(fill, a.steps)
+    step_us = timed(one_token, a.steps)
+    sb = storage_bits(bits)
+    partial = int((ctx % 16 != 0).sum())
+    byts = 2 * tokens * nkv * d * 2 + 2 * tokens * nkv * d * sb // 8
+    if quant:
+        byts += 2 * int((-(-ctx // 16)).sum()) * nkv * 2 + 2 * partial * nkv * 16 * d * 2
+    ms = wall * 1e3 / a.steps
+    k_avg = float(kern.mean())
+    res = {
+        "metric": "paged KV append (whole contexts through the block table): achieved HBM GB/s",
+        "value": round(byts / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {16: "bf16", 8: "bf16 -> int8", 4: "bf16 -> int4", PA_KV_FP8: "bf16 -> fp8 e4m3"}[bits],
+        "data": "synthetic",
+        "config": {"workload": CONFIGS[2]["workload"] + " [append of every context token in one call]",
+                   "tokens": tokens, "num_seqs": S, "n_kv_heads": nkv, "d_head": d, "kv_bits": bits},
+        "algorithmic_bytes_per_step": int(byts),
+        "roofline": {"bound": "hbm", "kernel": "kv_append_kernel", "achieved": round(byts / (k_avg * 1e-3) / 1e9, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(byts / (k_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel_avg_us": round(k_avg * 1e3, 3)},
+        "decode_step_append_us": round(float(np.median(step_us)) * 1e3, 2),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -394,6 +486,9 @@ def main():
         return
     if a.workload in ("5", "5p"):
         prefill_main(a, torch, B, CONFIGS)
+        return
+    if a.workload == "append":
+        append_main(a, torch, B, CONFIGS)
         return
     t_gen = time.perf_counter()
     case, kv_bits = build_case(a.workload)

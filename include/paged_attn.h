@@ -8,6 +8,8 @@
  *   paged_attn_prefill_chunk_window  the same over each row's last W tokens
  *   kv_quantize               symmetric int8 / int4 codes + fp16 scales
  *   paged_kv_write            scatter new tokens' K/V into their cache slots
+ *   paged_kv_append           append new tokens through the block table,
+ *                             quantizing on write for int8 / int4 / fp8 pools
  * plus a few host-only helpers (sizes, error strings).
  *
  * Sources (three web pages on KV caching, cited by title and section):
@@ -338,6 +340,49 @@ int kv_quantize(const void* src, void* codes, uint16_t* scales,
 int paged_kv_write(const void* k_src, const void* v_src, const int64_t* slot_mapping, int num_tokens,
                    void* k_pool, void* v_pool, int num_blocks, int block_size,
                    int n_kv_heads, int d_head, int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Append new tokens' keys/values through the block table ([TAI] "The KV
+ * cache": each step computes K/V only for the new tokens and appends them;
+ * [IR] "PagedAttention...": the table maps logical positions to physical
+ * blocks). Sequence s appends n_s = cu_new[s+1] - cu_new[s] tokens, rows
+ * cu_new[s] .. cu_new[s+1]-1 of k_new / v_new; they are its positions
+ * context_lens[s] - n_s .. context_lens[s] - 1 (context_lens holds the
+ * lengths after the append, as the decode takes them), and position t goes
+ * to slot t % 16 of block block_tables[s * max_blocks_per_seq + t / 16]. A
+ * decode step appends one token per sequence; a prefill chunk its tokens.
+ * k_new, v_new  [total_new][n_kv_heads][d_head] of dtype (either may be NULL)
+ * cu_new        int32 [num_seqs + 1] device prefix sums, 0 <= n_s <= max_new,
+ *               n_s <= context_lens[s]
+ * k_pool, v_pool  pools of kv_bits (written): 32 needs PA_F32, the others
+ *               PA_BF16. For 32 / 16 only the new tokens' elements are
+ *               written.
+ * Quantized pools (kv_bits 8, 4, PA_KV_FP8; [JE] "KV-cache quantization"):
+ * every block a call writes into gets the codes and fp16 scale that
+ * kv_quantize would give for the tokens written into it so far, the slots
+ * past the sequence's end counting as 0; so the block's scale is recomputed
+ * with every write and is final once the block holds 16 tokens. The earlier
+ * tokens of a partly filled block come from the sequence's staging tile:
+ * k_stage, v_stage  bf16 [num_seqs][n_kv_heads][16][d_head] (read and
+ *               written; NULL for 32 / 16). Row s holds, in slots
+ *               0 .. (context_lens[s] - n_s) % 16 - 1, the earlier tokens of
+ *               the block position context_lens[s] - n_s falls in; the call
+ *               leaves in it the tokens of the block position
+ *               context_lens[s] - 1 falls in, when that block is not full. The
+ *               caller keeps a sequence's row across calls (copying it with
+ *               the block on copy-on-write) and fills it for a sequence whose
+ *               cache was quantized by kv_quantize with a partly filled last
+ *               block.
+ * k_scales, v_scales  fp16 [num_blocks][n_kv_heads] (written; quantized only)
+ * Blocks a call writes must not be shared with another sequence of the same
+ * call (copy them on write first). Table entries outside [0, num_blocks) are
+ * recorded (pa_take_block_id_error) and nothing is written through them.
+ * ------------------------------------------------------------------------ */
+int paged_kv_append(const void* k_new, const void* v_new, const int32_t* cu_new, int total_new, int max_new,
+                    const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                    void* k_pool, void* v_pool, uint16_t* k_scales, uint16_t* v_scales,
+                    void* k_stage, void* v_stage, int num_seqs, int num_blocks, int block_size,
+                    int n_kv_heads, int d_head, int dtype, int kv_bits, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Copy whole blocks ([IR] "PagedAttention...": shared blocks are copied on

@@ -26,7 +26,7 @@ EXPORTS = (
     "pa_error_string", "pa_tile_bytes", "pa_kv_bytes_per_token", "pa_kv_cache_bytes",
     "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_decode_window", "paged_attn_prefill_chunk",
     "paged_attn_decode_noalloc", "paged_attn_prefill_chunk_window",
-    "kv_quantize", "paged_kv_write", "pa_copy_blocks", "pa_hbm_read_probe", "pa_take_block_id_error",
+    "kv_quantize", "paged_kv_write", "paged_kv_append", "pa_copy_blocks", "pa_hbm_read_probe", "pa_take_block_id_error",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_ref_count", "pa_bm_add", "pa_bm_append",
     "pa_bm_fork", "pa_bm_release", "pa_bm_num_tokens", "pa_bm_table",
     "pa_sched_create", "pa_sched_destroy", "pa_sched_submit", "pa_sched_num_live", "pa_sched_step",
@@ -70,6 +70,8 @@ def _declare(lib):
     lib.kv_quantize.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
     lib.paged_kv_write.restype = i
     lib.paged_kv_write.argtypes = [vp, vp, vp, i, vp, vp, i, i, i, i, i, vp]
+    lib.paged_kv_append.restype = i
+    lib.paged_kv_append.argtypes = [vp, vp, vp, i, i, vp, i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp]
     lib.pa_copy_blocks.restype = i
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp]
     lib.pa_hbm_read_probe.restype = i
@@ -303,6 +305,31 @@ def kv_write(k_src, v_src, slot_mapping, k_pool, v_pool, *, n_kv_heads, stream=N
     st = lib().paged_kv_write(_p(k_src), _p(v_src), _p(slot_mapping), T, _p(k_pool), _p(v_pool), nb, BLOCK_SIZE,
                               n_kv_heads, D, dt, _stream(stream, dev))
     _check("paged_kv_write", st)
+
+
+def kv_append(k_new, v_new, cu_new, block_tables, context_lens, k_pool, v_pool, *, n_kv_heads, max_new,
+              kv_bits=None, k_scales=None, v_scales=None, k_stage=None, v_stage=None, stream=None):
+    """paged_kv_append: k_new/v_new [T, n_kv, D] float32 or bfloat16 (either
+    may be None); cu_new [S+1] int32; context_lens [S] int32 (lengths after
+    the append). Quantized pools need their scales and bf16 staging tiles
+    [S, n_kv, 16, D]."""
+    src = k_new if k_new is not None else v_new
+    dev = _gpu(k_new, v_new, cu_new, block_tables, context_lens, k_pool, v_pool, k_scales, v_scales, k_stage,
+               v_stage)
+    T, _, D = src.shape
+    dt = _dtype_code(src.dtype)
+    if kv_bits is None:
+        kv_bits = 32 if dt == PA_F32 else 16
+    for t, name in ((cu_new, "cu_new"), (block_tables, "block_tables"), (context_lens, "context_lens")):
+        if t.dtype != torch.int32:
+            raise PagedAttnError(f"{name} must be int32")
+    nb = _num_blocks(k_pool if k_pool is not None else v_pool, n_kv_heads, D, kv_bits)
+    S = context_lens.shape[0]
+    st = lib().paged_kv_append(_p(k_new), _p(v_new), _p(cu_new), T, int(max_new), _p(block_tables),
+                               block_tables.shape[1], _p(context_lens), _p(k_pool), _p(v_pool), _p(k_scales),
+                               _p(v_scales), _p(k_stage), _p(v_stage), S, nb, BLOCK_SIZE, n_kv_heads, D, dt, kv_bits,
+                               _stream(stream, dev))
+    _check("paged_kv_append", st)
 
 
 def copy_blocks(pairs, k_pool, v_pool, *, n_kv_heads, d_head, kv_bits, k_scales=None, v_scales=None, stream=None):

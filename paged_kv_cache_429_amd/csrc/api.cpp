@@ -419,6 +419,31 @@ int pa_copy_blocks(void* k_pool, void* v_pool, uint16_t* k_scales, uint16_t* v_s
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+int paged_kv_append(const void* k_new, const void* v_new, const int32_t* cu_new, int total_new, int max_new,
+                    const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                    void* k_pool, void* v_pool, uint16_t* k_scales, uint16_t* v_scales, void* k_stage,
+                    void* v_stage, int num_seqs, int num_blocks, int block_size, int n_kv_heads, int d_head,
+                    int dtype, int kv_bits, void* stream) {
+    if (num_seqs < 0 || num_blocks <= 0 || block_size != PA_BLOCK_SIZE || n_kv_heads <= 0 || d_head <= 0)
+        return PA_ERR_INVALID_ARG;
+    if (total_new < 0 || max_new < 0 || max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
+    if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_INVALID_ARG;
+    if (!valid_kv_bits(kv_bits)) return PA_ERR_INVALID_ARG;
+    const int fmt = fmt_of(dtype, kv_bits);
+    if (fmt < 0) return PA_ERR_UNSUPPORTED;
+    if (d_head != 64 && d_head != 128) return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || total_new == 0 || max_new == 0 || (!k_new && !v_new)) return PA_OK;
+    if (!cu_new || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+    const bool q = quantized(kv_bits);
+    if (k_new && (!k_pool || (q && (!k_scales || !k_stage)))) return PA_ERR_INVALID_ARG;
+    if (v_new && (!v_pool || (q && (!v_scales || !v_stage)))) return PA_ERR_INVALID_ARG;
+    const hipError_t e = pa::launch_kv_append(k_new, v_new, cu_new, max_new, block_tables, max_blocks_per_seq,
+                                              context_lens, k_pool, v_pool, k_scales, v_scales, k_stage, v_stage,
+                                              num_seqs, num_blocks, n_kv_heads, d_head, fmt,
+                                              static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 int pa_take_block_id_error(int64_t* table_index, int32_t* block_id) {
     pa::BadIdRecord r[3] = {};
     if (pa::take_bad_id_decode(&r[0]) != hipSuccess || pa::take_bad_id_prefill(&r[1]) != hipSuccess ||

@@ -44,6 +44,38 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float r) {
     return sign | mag;
 }
 
+// Scale of a tile whose largest magnitude is amax: the fp16 value nearest
+// amax / qmax (IEEE float32 division, then round to nearest even), with
+// qmax 127 / 7 / 448 for BITS 8 / 4 / 0 (fp8). Returns its float32 value;
+// *bits gets its fp16 bit pattern; *zero is set when every code of the tile
+// is 0 (scale 0, or for fp8 an infinite scale).
+template <int BITS>
+__device__ __forceinline__ float tile_scale(float amax, uint16_t* bits, bool* zero) {
+    constexpr float qmax = BITS == 0 ? 448.f : (BITS == 8) ? 127.f : 7.f;
+    const float s32 = amax / qmax;
+    const _Float16 s16 = (_Float16)s32;
+    const float sf = (float)s16;
+    *bits = __builtin_bit_cast(uint16_t, s16);
+    *zero = !(sf > 0.f) || (BITS == 0 && __builtin_isinf(sf));
+    return sf;
+}
+
+// Code of x under the tile scale sf: clamp(rint(x / sf), -qmax, qmax) for
+// integer codes, the e4m3 code nearest x / sf for fp8 (BITS 0); 0 if zero.
+template <int BITS>
+__device__ __forceinline__ int quant_code(float x, float sf, bool zero) {
+    if (zero) return 0;
+    const float r = x / sf;
+    if constexpr (BITS == 0) {
+        return (int)f32_to_e4m3(r);
+    } else {
+        constexpr float qmax = (BITS == 8) ? 127.f : 7.f;
+        float c = __builtin_rintf(r);
+        c = fminf(fmaxf(c, -qmax), qmax);
+        return (int)c;
+    }
+}
+
 // BITS 8 or 4 (integer codes) or 0 (fp8 e4m3 codes, one byte each).
 template <int D, int BITS, int KIND>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ src, uint8_t* __restrict__ codes,
@@ -64,15 +96,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
 
-    constexpr bool F8 = (BITS == 0);
-    constexpr int CB = F8 ? 8 : BITS;              // bits per code
-    constexpr float qmax = F8 ? 448.f : (BITS == 8) ? 127.f : 7.f;
-    const float s32 = amax / qmax;                 // IEEE division
-    const _Float16 s16 = (_Float16)s32;            // round to nearest even
-    const float sf = (float)s16;
-    if (lane == 0) scales[(size_t)b * n_kv + h] = __builtin_bit_cast(uint16_t, s16);
-    // s == 0 (and, for fp8, s == inf): all codes 0
-    const bool zero = !(sf > 0.f) || (F8 && __builtin_isinf(sf));
+    constexpr int CB = BITS == 0 ? 8 : BITS;       // bits per code
+    uint16_t sbits;
+    bool zero;
+    const float sf = tile_scale<BITS>(amax, &sbits, &zero);
+    if (lane == 0) scales[(size_t)b * n_kv + h] = sbits;
 
     auto code_of = [&](int n) -> int {
         // element n of the int tile -> (slot, dim) -> source element
@@ -87,15 +115,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
             tt = n % 16;
         }
         const int se = (KIND == 0) ? k_elem(tt, ii, 8) : ii * 16 + tt;
-        if (zero) return 0;
-        const float r = bf16_bits_to_f32(t[se]) / sf;
-        if constexpr (F8) {
-            return (int)f32_to_e4m3(r);
-        } else {
-            float c = __builtin_rintf(r);
-            c = fminf(fmaxf(c, -qmax), qmax);
-            return (int)c;
-        }
+        return quant_code<BITS>(bf16_bits_to_f32(t[se]), sf, zero);
     };
 
     uint8_t* out = codes + ((size_t)b * n_kv + h) * (N * CB / 8);
@@ -197,6 +217,225 @@ hipError_t launch_kv_write(const void* k_src, const void* v_src, const int64_t* 
     if (d == 128 && eb == 4) return write_t<128, 4>(k_src, v_src, slots, num_tokens, k_pool, v_pool, num_blocks, n_kv, stream);
     if (d == 64 && eb == 2) return write_t<64, 2>(k_src, v_src, slots, num_tokens, k_pool, v_pool, num_blocks, n_kv, stream);
     if (d == 64 && eb == 4) return write_t<64, 4>(k_src, v_src, slots, num_tokens, k_pool, v_pool, num_blocks, n_kv, stream);
+    return hipErrorInvalidValue;
+}
+
+// -----------------------------------------------------------------------------
+// Append through the block table. Sequence s's new tokens are its last n_s
+// positions, ctx_s - n_s .. ctx_s - 1 (rows cu[s] .. cu[s+1]-1 of the
+// source); the token at position t goes to slot t % 16 of physical block
+// table[s][t / 16]. One wave per (sequence, touched block, KV head, K or V):
+// it assembles the block's tile in LDS as 16 slots x D float32 values (the
+// new tokens; for a quantized pool also the block's earlier tokens, kept in
+// the sequence's bf16 staging tile, and 0 for the slots past the end), then
+// writes the tile in the pool's layout with 16-byte stores. A plain pool gets
+// only the new tokens' elements; a quantized pool gets the whole tile's codes
+// and its scale, recomputed from every token written so far, and the
+// staging tile keeps the new tokens of a block left partly filled.
+// -----------------------------------------------------------------------------
+struct AppendParams {
+    const uint8_t* src[2];   // K, V new rows [total][n_kv][D] (bf16 or f32); null = skip
+    uint8_t* pool[2];
+    uint16_t* scales[2];     // quantized pools
+    uint16_t* stage[2];      // bf16 [num_seqs][n_kv][16][D], quantized pools
+    const int32_t* cu;
+    const int32_t* ctx;
+    const int32_t* tables;
+    int max_blocks;
+    int num_blocks;
+    int n_kv;
+    int tiles_per_seq;       // blocks a sequence's new tokens can touch
+};
+
+// FMT: FMT_F32 / FMT_BF16 (plain pools of that element type) or FMT_I8 /
+// FMT_I4 / FMT_F8 (quantized pools, bf16 source).
+template <int D, int FMT>
+__global__ __launch_bounds__(64) void kv_append_kernel(AppendParams p) {
+    constexpr bool QUANT = is_quant<FMT>();
+    constexpr int SEB = FMT == FMT_F32 ? 4 : 2;            // source element bytes
+    constexpr int CB = FmtBits<FMT>::v;                    // pool bits per element
+    constexpr int BITS = FMT == FMT_F8 ? 0 : CB;           // quant_code selector
+    constexpr int TILE = 16 * D * CB / 8;                  // pool bytes of one tile
+    constexpr int EPC = 128 / CB;                          // elements per 16-byte pool chunk
+    __shared__ float tile[16][D + 1];
+
+    const int lane = threadIdx.x;
+    const int kind = blockIdx.x & 1;
+    int rest = blockIdx.x >> 1;
+    const int kvh = rest % p.n_kv;
+    rest /= p.n_kv;
+    const int q = rest % p.tiles_per_seq;
+    const int s = rest / p.tiles_per_seq;
+    const uint8_t* src = p.src[kind];
+    if (!src) return;
+    const int row0 = p.cu[s];
+    const int n = p.cu[s + 1] - row0;
+    const int ctx = p.ctx[s];
+    const int first = ctx - n;  // first new position
+    if (n <= 0 || first < 0) return;
+    const int j = first / kBlock + q;  // logical block
+    if (j > (ctx - 1) / kBlock) return;
+    const long tidx = (long)s * p.max_blocks + j;
+    const int phys = p.tables[tidx];
+    if ((unsigned)phys >= (unsigned)p.num_blocks) {  // never written through: recorded instead
+        if (lane == 0) note_bad_id(tidx, phys);
+        return;
+    }
+    const int lo = max(first - kBlock * j, 0);      // new slots [lo, hi)
+    const int hi = min(ctx - kBlock * j, kBlock);
+    uint16_t* stage = QUANT ? p.stage[kind] + ((size_t)s * p.n_kv + kvh) * kBlock * D : nullptr;
+
+    // the tile's values: 16-byte pieces of the source rows (or staging)
+    constexpr int SPP = 16 / SEB;                           // source elements per piece
+    for (int c = lane; c < kBlock * D / SPP; c += 64) {
+        const int t = c / (D / SPP);
+        const int i0 = (c % (D / SPP)) * SPP;
+        float v[SPP];
+        if (t >= lo && t < hi) {
+            const size_t row = (size_t)row0 + kBlock * j + t - first;
+            const u32x4 w = *reinterpret_cast<const u32x4*>(src + ((row * p.n_kv + kvh) * D + i0) * SEB);
+#pragma unroll
+            for (int e = 0; e < SPP; ++e) {
+                v[e] = SEB == 4 ? __uint_as_float(w[e]) : bf16_bits_to_f32((w[e / 2] >> (16 * (e % 2))) & 0xffffu);
+            }
+        } else if (QUANT && t < lo) {  // written by an earlier call: kept in the staging tile
+            const u32x4 w = *reinterpret_cast<const u32x4*>(stage + t * D + i0);
+#pragma unroll
+            for (int e = 0; e < SPP; ++e) v[e] = bf16_bits_to_f32((w[e / 2] >> (16 * (e % 2))) & 0xffffu);
+        } else {
+#pragma unroll
+            for (int e = 0; e < SPP; ++e) v[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < SPP; ++e) tile[t][i0 + e] = v[e];
+    }
+    __syncthreads();
+
+    // (slot, dim) of element number el of the tile in the pool's layout
+    auto elem = [&](int el, int& t, int& i) {
+        if (kind == 0) {  // K: 16-byte chunks of EPC consecutive dims, slot-minor
+            const int ch = el / (16 * EPC);
+            t = (el / EPC) % 16;
+            i = ch * EPC + el % EPC;
+        } else {          // V: transposed, dim-major
+            i = el / 16;
+            t = el % 16;
+        }
+    };
+    uint8_t* out = p.pool[kind] + ((size_t)phys * p.n_kv + kvh) * TILE;
+
+    if constexpr (!QUANT) {
+        for (int k = lane; k < TILE / 16; k += 64) {
+            u32x4 w;
+            int n_new = 0;
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) {
+                int t, i;
+                elem(k * EPC + e, t, i);
+                n_new += (t >= lo && t < hi);
+            }
+            if (n_new == 0) continue;
+            if (n_new == EPC) {
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) {
+                    int t, i;
+                    elem(k * EPC + e, t, i);
+                    const float x = tile[t][i];
+                    if (SEB == 4) {
+                        w[e] = __float_as_uint(x);
+                    } else if (e % 2 == 0) {
+                        w[e / 2] = __float_as_uint(x) >> 16;
+                    } else {
+                        w[e / 2] |= __float_as_uint(x) & 0xffff0000u;
+                    }
+                }
+                *reinterpret_cast<u32x4*>(out + (size_t)k * 16) = w;
+            } else {  // a chunk shared with slots not written now: its new elements one by one
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) {
+                    int t, i;
+                    elem(k * EPC + e, t, i);
+                    if (t < lo || t >= hi) continue;
+                    const float x = tile[t][i];
+                    if (SEB == 4) {
+                        reinterpret_cast<uint32_t*>(out)[k * EPC + e] = __float_as_uint(x);
+                    } else {
+                        reinterpret_cast<uint16_t*>(out)[k * EPC + e] = (uint16_t)(__float_as_uint(x) >> 16);
+                    }
+                }
+            }
+        }
+    } else {
+        float amax = 0.f;
+        for (int e = lane; e < kBlock * D; e += 64) amax = fmaxf(amax, fabsf(tile[e / D][e % D]));
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+        uint16_t sbits;
+        bool zero;
+        const float sf = tile_scale<BITS>(amax, &sbits, &zero);
+        if (lane == 0) p.scales[kind][(size_t)phys * p.n_kv + kvh] = sbits;
+        for (int k = lane; k < TILE / 16; k += 64) {
+            u32x4 w = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) {
+                int t, i;
+                elem(k * EPC + e, t, i);
+                const uint32_t c = (uint32_t)quant_code<BITS>(tile[t][i], sf, zero) & ((1u << CB) - 1u);
+                w[(e * CB) / 32] |= c << ((e * CB) % 32);
+            }
+            *reinterpret_cast<u32x4*>(out + (size_t)k * 16) = w;
+        }
+        // a block left partly filled keeps its new tokens for the next write
+        if (j == (ctx - 1) / kBlock && ctx % kBlock != 0) {
+            for (int c = lane; c < (hi - lo) * D / 8; c += 64) {
+                const int t = lo + c / (D / 8);
+                const int i0 = (c % (D / 8)) * 8;
+                u32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    w[e] = (__float_as_uint(tile[t][i0 + 2 * e]) >> 16) |
+                           (__float_as_uint(tile[t][i0 + 2 * e + 1]) & 0xffff0000u);
+                }
+                *reinterpret_cast<u32x4*>(stage + t * D + i0) = w;
+            }
+        }
+    }
+}
+
+template <int D, int FMT>
+static hipError_t append_t(const AppendParams& p, int num_seqs, hipStream_t stream) {
+    const long grid = (long)num_seqs * p.tiles_per_seq * p.n_kv * 2;
+    if (grid == 0) return hipSuccess;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((kv_append_kernel<D, FMT>), dim3((unsigned)grid), dim3(64), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, const int32_t* cu_new, int max_new,
+                            const int32_t* tables, int max_blocks, const int32_t* ctx, void* k_pool, void* v_pool,
+                            uint16_t* k_scales, uint16_t* v_scales, void* k_stage, void* v_stage, int num_seqs,
+                            int num_blocks, int n_kv, int d, int fmt, hipStream_t stream) {
+    AppendParams p{};
+    p.src[0] = static_cast<const uint8_t*>(k_new);
+    p.src[1] = static_cast<const uint8_t*>(v_new);
+    p.pool[0] = static_cast<uint8_t*>(k_pool);
+    p.pool[1] = static_cast<uint8_t*>(v_pool);
+    p.scales[0] = k_scales;
+    p.scales[1] = v_scales;
+    p.stage[0] = static_cast<uint16_t*>(k_stage);
+    p.stage[1] = static_cast<uint16_t*>(v_stage);
+    p.cu = cu_new;
+    p.ctx = ctx;
+    p.tables = tables;
+    p.max_blocks = max_blocks;
+    p.num_blocks = num_blocks;
+    p.n_kv = n_kv;
+    p.tiles_per_seq = (max_new + kBlock - 1) / kBlock + 1;
+#define PA_A(DD, FF) \
+    if (d == DD && fmt == FF) return append_t<DD, FF>(p, num_seqs, stream);
+    PA_A(128, FMT_F32) PA_A(128, FMT_BF16) PA_A(128, FMT_I8) PA_A(128, FMT_I4) PA_A(128, FMT_F8)
+    PA_A(64, FMT_F32) PA_A(64, FMT_BF16) PA_A(64, FMT_I8) PA_A(64, FMT_I4) PA_A(64, FMT_F8)
+#undef PA_A
     return hipErrorInvalidValue;
 }
 

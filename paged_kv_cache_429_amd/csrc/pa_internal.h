@@ -168,6 +168,11 @@ hipError_t launch_copy_blocks(void* k_pool, void* v_pool, uint16_t* k_scales, ui
 hipError_t launch_read_probe(const void* buf, long buf_tiles, long n_tiles, int tile_bytes, const int32_t* order,
                              uint32_t* xor_out, int grid, hipStream_t stream);
 
+hipError_t launch_kv_append(const void* k_new, const void* v_new, const int32_t* cu_new, int max_new,
+                            const int32_t* tables, int max_blocks, const int32_t* ctx, void* k_pool, void* v_pool,
+                            uint16_t* k_scales, uint16_t* v_scales, void* k_stage, void* v_stage, int num_seqs,
+                            int num_blocks, int n_kv, int d, int fmt, hipStream_t stream);
+
 hipError_t launch_kv_write(const void* k_src, const void* v_src, const int64_t* slots, int num_tokens,
                            void* k_pool, void* v_pool, int num_blocks, int n_kv, int d, int fmt,
                            hipStream_t stream);
