@@ -78,6 +78,10 @@
  *     K pool:  ((i / x) * 16 + t) * x + i % x,   x = 128 / bits
  *              (16-byte chunks of x consecutive dims, slot-minor)
  *     V pool:  i * 16 + t                          (transposed: dim-major)
+ *              for kv_bits 32, 16, 8 and PA_KV_FP8; for kv_bits 4
+ *              (((i % 16) * 2 + t / 8) * (d_head / 16) + i / 16) * 8 + t % 8
+ *              (runs of 8 consecutive slots of one dim; the d_head / 16 runs
+ *              of dims i % 16 and slots t / 8 side by side)
  * of the tile, elements packed at kv_bits each, little-endian; for int4 the
  * even-numbered element of a pair is the low nibble. Integer codes are two's
  * complement. Scales are float16 bit patterns, k_scales / v_scales

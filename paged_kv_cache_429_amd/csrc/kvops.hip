@@ -23,6 +23,24 @@ namespace pa {
 // element number of (slot t, dim i) inside a K tile, x elements per 16 bytes
 __device__ __forceinline__ int k_elem(int t, int i, int x) { return ((i / x) * 16 + t) * x + i % x; }
 
+// (slot t, dim i) of element number n of a V tile of D dims at CB bits per
+// element: i * 16 + t (transposed, dim-major), except int4, whose element
+// (t, i) is number (((i % 16) * 2 + t / 8) * (D / 16) + i / 16) * 8 + t % 8:
+// runs of 8 tokens of one dim, those a decode lane reads (the same i % 16
+// and token half, every dim block) side by side.
+template <int D, int CB>
+__device__ __forceinline__ void v_elem(int n, int& t, int& i) {
+    if constexpr (CB == 4) {
+        constexpr int NB = D / 16;
+        const int rest = n / (8 * NB);
+        i = ((n / 8) % NB) * 16 + rest / 2;
+        t = (rest % 2) * 8 + n % 8;
+    } else {
+        i = n / 16;
+        t = n % 16;
+    }
+}
+
 // e4m3 code of float32 r (finite): magnitudes from 448 up saturate to 448
 // (0x7E); below the smallest normal 2^-6 the code is the multiple of 2^-9
 // nearest |r| (rint of |r| * 512, exact, 0..8, where 8 is 2^-6's code);
@@ -111,8 +129,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
             tt = (n / x) % 16;
             ii = c * x + n % x;
         } else {
-            ii = n / 16;
-            tt = n % 16;
+            v_elem<D, CB>(n, tt, ii);
         }
         const int se = (KIND == 0) ? k_elem(tt, ii, 8) : ii * 16 + tt;
         return quant_code<BITS>(bf16_bits_to_f32(t[se]), sf, zero);
@@ -317,9 +334,8 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AppendParams p) {
             const int ch = el / (16 * EPC);
             t = (el / EPC) % 16;
             i = ch * EPC + el % EPC;
-        } else {          // V: transposed, dim-major
-            i = el / 16;
-            t = el % 16;
+        } else {          // V: transposed (int4: in runs of 8 tokens, see v_elem)
+            v_elem<D, CB>(el, t, i);
         }
     };
     uint8_t* out = p.pool[kind] + ((size_t)phys * p.n_kv + kvh) * TILE;

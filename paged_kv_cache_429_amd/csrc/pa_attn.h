@@ -182,16 +182,19 @@ struct Mfma {
                 r.w[2 * nb + 1] = v[1];
             } else if (FMT == FMT_I8 || FMT == FMT_F8) {
                 r.w[nb] = ld<NT>(reinterpret_cast<const uint32_t*>(tile + d * 16 + q * 4));
-            } else {
-                r.w[nb] = ld<NT>(reinterpret_cast<const uint16_t*>(tile + d * 8 + q * 2));
+            } else {  // int4: tokens 4q..4q+3 of dim d, in the 8-token piece (d % 16, q / 2, nb)
+                r.w[nb] = ld<NT>(reinterpret_cast<const uint16_t*>(tile + ((l16 * 2 + q / 2) * NB + nb) * 4 +
+                                                                   (q % 2) * 2));
             }
         }
     }
 
     // V operand of a pair for the decode P.V product: lane (l16, q) holds,
     // for dim row nb*16 + l16, the 8 consecutive tokens 8 (q % 2) .. + 7 of
-    // the pair's block q / 2 -- one contiguous run of a V tile row (16, 8 or
-    // 4 bytes), so each load instruction moves 1 KiB, 512 B or 256 B.
+    // the pair's block q / 2 -- one contiguous run of a V tile row (16 or 8
+    // bytes for bf16 and int8 / fp8, so each load instruction moves 1 KiB or
+    // 512 B). An int4 tile keeps the NB 4-byte runs a lane needs next to each
+    // other, so it loads all of them as 4 NB contiguous bytes.
     static constexpr int VPDW = (FMT == FMT_BF16) ? 4 : (FMT == FMT_I8 || FMT == FMT_F8 ? 2 : 1);  // dwords per nb
     struct VPairRaw { uint32_t w[NB * VPDW]; };
 
@@ -214,8 +217,17 @@ struct Mfma {
                 const u32x2 v = ld<NT>(reinterpret_cast<const u32x2*>(a));
                 r.w[2 * nb] = v[0];
                 r.w[2 * nb + 1] = v[1];
-            } else {
-                r.w[nb] = ld<NT>(reinterpret_cast<const uint32_t*>(a));
+            }
+        }
+        if constexpr (FMT == FMT_I4) {  // the lane's NB runs: piece (l16, q % 2) of the tile
+            const uint8_t* a = t + (l16 * 2 + (q & 1)) * NB * 4;
+#pragma unroll
+            for (int u = 0; u < NB / 4; ++u) {
+                const u32x4 v = ld<NT>(reinterpret_cast<const u32x4*>(a + 16 * u));
+                r.w[4 * u + 0] = v[0];
+                r.w[4 * u + 1] = v[1];
+                r.w[4 * u + 2] = v[2];
+                r.w[4 * u + 3] = v[3];
             }
         }
     }

@@ -6,7 +6,7 @@ them back. Written from the header's formula, independently of the kernels:
   tile_bytes = 16 * d * bits / 8; inside a tile element (slot t, dim i) is
   element number
       K: ((i // x) * 16 + t) * x + i % x,   x = 128 // bits
-      V: i * 16 + t
+      V: i * 16 + t   (int4: (((i % 16) * 2 + t // 8) * (d // 16) + i // 16) * 8 + t % 8)
   packed at `bits` each, little-endian; int4 pairs put the even element in
   the low nibble.
 """
@@ -20,6 +20,8 @@ def elem_index(kind: str, d: int, bits: int) -> np.ndarray:
     if kind == "k":
         x = 128 // bits
         return ((i // x) * 16 + t) * x + i % x
+    if bits == 4:
+        return (((i % 16) * 2 + t // 8) * (d // 16) + i // 16) * 8 + t % 8
     return i * 16 + t + 0 * t
 
 

@@ -17,6 +17,10 @@ def test_hand_computed_offsets():
     assert elem_index("k", 128, 32)[15, 127] == (31 * 16 + 15) * 4 + 3
     # int8 K: x = 16, (t=0, i=17) -> (16 + 0)*16 + 1
     assert elem_index("k", 128, 8)[0, 17] == 257
+    # int4 V, d 128 (8 dim blocks): (t=9, i=37) -> (((5*2 + 1) * 8) + 2) * 8 + 1
+    assert elem_index("v", 128, 4)[9, 37] == 721
+    # int4 V, d 64 (4 dim blocks): (t=7, i=63) -> (((15*2 + 0) * 4) + 3) * 8 + 7
+    assert elem_index("v", 64, 4)[7, 63] == 991
 
 
 @pytest.mark.parametrize("kind", ["k", "v"])
