@@ -12,9 +12,13 @@ before timing; steps cycle through several identical copies of the layer's
 pools (as a model's layers would) so that consecutive steps do not re-read
 the same memory from the last-level cache.
 
-Timing: after the warm-up, K steps run back to back for the wall-clock
-value, then the same K steps again, each bracketed by HIP events on its
-stream, for the kernel time of the roofline.
+Timing: after the warm-up, K steps run back to back; the wall clock around
+them gives the line's value, and HIP events recorded on the launch stream
+at the start and end of the same timed region give the kernel time of the
+roofline (their span / K, launch gaps between the steps included). The
+default line (workload 2) also times the other two bf16 decode workloads,
+the 70B-class prefix-shared layer and the mixed step's decode half, the
+same way, under "other_bf16_decode".
 
 The line also carries the device's measured read ceiling (the library's
 read probe: random 4 KiB tiles, and a stream) and the decode's fraction of
@@ -66,6 +70,9 @@ def parse():
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window in tokens for the decode workloads (0: full attention)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="workload 2 only: skip timing the other bf16 decode workloads (70B prefix-shared, "
+                         "mixed-step decode half) beside it")
     ap.add_argument("--no-read-probe", action="store_true",
                     help="skip measuring the device's read ceiling (random 4 KiB tiles and a stream)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -331,27 +338,23 @@ def prefill_main(a, torch, B, CONFIGS):
             s_main.wait_stream(s_dec)
 
     def timed(n):
-        # wall-clock pass: n steps back to back; then a kernel pass of n
-        # steps, each bracketed by events on the main stream
+        # n steps back to back: the wall clock around them, and HIP events on
+        # the main stream at the start and end of the same region
         torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        e0.record(s_main)
         for _ in range(n):
             step()
+        e1.record(s_main)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        for i in range(n):
-            ev[i][0].record(s_main)
-            step()
-            ev[i][1].record(s_main)
-        torch.cuda.synchronize()
-        return wall, np.array([x.elapsed_time(y) for x, y in ev])
+        return time.perf_counter() - t0, e0.elapsed_time(e1)
 
     for _ in range(a.warmup):
         step()
-    wall, kern_ms = timed(a.steps)
+    wall, ev_ms = timed(a.steps)
     flops = prefill_flops(pre)
-    k_avg = float(kern_ms.mean())
+    k_avg = ev_ms / a.steps
     ms_step = wall * 1e3 / a.steps
     res = {
         "metric": "causal chunked-prefill attention: achieved MFMA TFLOP/s (% of bf16 dense peak)"
@@ -423,34 +426,30 @@ def append_main(a, torch, B, CONFIGS):
                     k_scales=ks, v_scales=vs, k_stage=kst, v_stage=vst)
 
     def timed(fn, n):
+        # n calls back to back: the wall clock around them, and HIP events on
+        # the stream at the start and end of the same region (ms per call)
         stream = torch.cuda.current_stream()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        for i in range(n):
-            ev[i][0].record(stream)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(n):
             fn()
-            ev[i][1].record(stream)
+        e1.record(stream)
         torch.cuda.synchronize()
-        return np.array([x.elapsed_time(y) for x, y in ev])
+        return time.perf_counter() - t0, e0.elapsed_time(e1) / n
 
     for _ in range(a.warmup):
         fill()
         one_token()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(a.steps):
-        fill()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern = timed(fill, a.steps)
-    step_us = timed(one_token, a.steps)
+    wall, k_avg = timed(fill, a.steps)
+    _, step_ms = timed(one_token, a.steps)
     sb = storage_bits(bits)
     partial = int((ctx % 16 != 0).sum())
     byts = 2 * tokens * nkv * d * 2 + 2 * tokens * nkv * d * sb // 8
     if quant:
         byts += 2 * int((-(-ctx // 16)).sum()) * nkv * 2 + 2 * partial * nkv * 16 * d * 2
     ms = wall * 1e3 / a.steps
-    k_avg = float(kern.mean())
     res = {
         "metric": "paged KV append (whole contexts through the block table): achieved HBM GB/s",
         "value": round(byts / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps,
@@ -465,9 +464,79 @@ def append_main(a, torch, B, CONFIGS):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(byts / (k_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel_avg_us": round(k_avg * 1e3, 3)},
-        "decode_step_append_us": round(float(np.median(step_us)) * 1e3, 2),
+        "decode_step_append_us": round(step_ms * 1e3, 2),
     }
     print(json.dumps(res), flush=True)
+
+
+def measure_decode(torch, B, case, kv_bits, steps, warmup, n_layers, partition_blocks=0, window=0):
+    """Device pools for the case (one copy written by paged_kv_write,
+    quantized if asked, replicated for n_layers layers that the steps cycle
+    through), then `warmup` steps and `steps` timed steps back to back.
+    Returns (wall seconds of the timed steps, milliseconds between HIP events
+    recorded on the launch stream at the start and end of the same timed
+    region)."""
+    src_bits = 32 if case.dtype == "f32" else 16
+    kp = B.alloc_pool(case.num_blocks, case.n_kv, case.d, src_bits)
+    vp = B.alloc_pool(case.num_blocks, case.n_kv, case.d, src_bits)
+    slots = torch.arange(case.num_blocks * 16, dtype=torch.int64, device="cuda")
+    B.kv_write(to_dev(case.k_slots, case.dtype, torch), to_dev(case.v_slots, case.dtype, torch), slots, kp, vp,
+               n_kv_heads=case.n_kv)
+    ks = vs = None
+    if storage_bits(kv_bits) < 16:
+        kp, ks = B.quantize(kp, bits=kv_bits, kind=0, n_kv_heads=case.n_kv, d_head=case.d)
+        vp, vs = B.quantize(vp, bits=kv_bits, kind=1, n_kv_heads=case.n_kv, d_head=case.d)
+    layers = [(kp, vp, ks, vs)]
+    for _ in range(n_layers - 1):
+        layers.append(tuple(None if t is None else t.clone() for t in (kp, vp, ks, vs)))
+    q = to_dev(case.q, case.dtype, torch)
+    tables = torch.from_numpy(np.ascontiguousarray(case.block_tables)).cuda()
+    ctx = torch.from_numpy(np.ascontiguousarray(case.context_lens)).cuda()
+    out = torch.empty_like(q)
+    mcl = case.max_context_len
+    ws = B.decode_workspace(case.num_seqs, case.n_heads, case.n_kv, case.d, mcl, partition_blocks)
+    torch.cuda.synchronize()
+
+    def step(i):
+        k_, v_, ks_, vs_ = layers[i % len(layers)]
+        B.decode(q, k_, v_, tables, ctx, n_kv_heads=case.n_kv, max_context_len=mcl, kv_bits=kv_bits,
+                 k_scales=ks_, v_scales=vs_, out=out, workspace=ws, partition_blocks=partition_blocks,
+                 window=window or None)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = t_start.elapsed_time(t_end)
+    del layers, kp, vp, ks, vs, ws
+    return wall, ev_ms
+
+
+def extra_decode_configs(torch, B, steps, warmup, n_layers):
+    """The other bf16 decode workloads, timed the same way: the 70B-class
+    prefix-shared layer and the decode half of the mixed step."""
+    out = {}
+    for wl, key in (("3", "prefix_shared_70b_bf16"), ("5d", "mixed_step_decode_bf16")):
+        case, kv_bits = build_case(wl)
+        wall, ev_ms = measure_decode(torch, B, case, kv_bits, steps, warmup, n_layers)
+        byts = decode_bytes(case, kv_bits)
+        k_us = ev_ms * 1e3 / steps
+        out[key] = {"workload": wl, "us_per_step": round(wall * 1e6 / steps, 3), "kernel_avg_us": round(k_us, 3),
+                    "GBps": round(byts / (k_us * 1e-6) / 1e9, 2),
+                    "frac": round(byts / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "tokens_per_s_per_layer": round(case.num_seqs / (wall / steps), 1),
+                    "algorithmic_bytes_per_step": int(byts)}
+        del case
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -493,62 +562,12 @@ def main():
     t_gen = time.perf_counter()
     case, kv_bits = build_case(a.workload)
     gen_s = time.perf_counter() - t_gen
-
-    # device pools: one bf16 copy written by paged_kv_write, quantized if asked,
-    # then replicated for `layers` layers
-    src_bits = 32 if case.dtype == "f32" else 16
-    kp = B.alloc_pool(case.num_blocks, case.n_kv, case.d, src_bits)
-    vp = B.alloc_pool(case.num_blocks, case.n_kv, case.d, src_bits)
-    slots = torch.arange(case.num_blocks * 16, dtype=torch.int64, device="cuda")
-    B.kv_write(to_dev(case.k_slots, case.dtype, torch), to_dev(case.v_slots, case.dtype, torch), slots, kp, vp,
-               n_kv_heads=case.n_kv)
-    ks = vs = None
-    if storage_bits(kv_bits) < 16:
-        kp, ks = B.quantize(kp, bits=kv_bits, kind=0, n_kv_heads=case.n_kv, d_head=case.d)
-        vp, vs = B.quantize(vp, bits=kv_bits, kind=1, n_kv_heads=case.n_kv, d_head=case.d)
-    layers = [(kp, vp, ks, vs)]
-    for _ in range(a.layers - 1):
-        layers.append(tuple(None if t is None else t.clone() for t in (kp, vp, ks, vs)))
-    q = to_dev(case.q, case.dtype, torch)
-    tables = torch.from_numpy(np.ascontiguousarray(case.block_tables)).cuda()
-    ctx = torch.from_numpy(np.ascontiguousarray(case.context_lens)).cuda()
-    out = torch.empty_like(q)
+    wall, ev_ms = measure_decode(torch, B, case, kv_bits, a.steps, a.warmup, a.layers, a.partition_blocks, a.window)
     mcl = case.max_context_len
-    ws = B.decode_workspace(case.num_seqs, case.n_heads, case.n_kv, case.d, mcl, a.partition_blocks)
-    torch.cuda.synchronize()
-
-    def step(i):
-        k_, v_, ks_, vs_ = layers[i % len(layers)]
-        B.decode(q, k_, v_, tables, ctx, n_kv_heads=case.n_kv, max_context_len=mcl, kv_bits=kv_bits,
-                 k_scales=ks_, v_scales=vs_, out=out, workspace=ws, partition_blocks=a.partition_blocks,
-                 window=a.window or None)
-
-    for i in range(a.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    # wall-clock pass (the line's value): K steps back to back
-    t0 = time.perf_counter()
-    for i in range(a.steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # kernel pass (the roofline): the same K steps, each bracketed by HIP
-    # events on its stream (recording them costs time between steps, so it
-    # is kept out of the wall-clock pass)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
-    torch.cuda.synchronize()
-    for i in range(a.steps):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    kern_ms = np.array([s.elapsed_time(e) for s, e in ev])
-
     byts = decode_bytes(case, kv_bits, a.window)
     ms_step = wall * 1e3 / a.steps
     value = byts / (ms_step * 1e-3) / 1e9
-    k_avg = float(kern_ms.mean())
+    k_avg = ev_ms / a.steps
     achieved = byts / (k_avg * 1e-3) / 1e9
     name = {"2": 2, "3": 3, "4a": 4, "4b": 4, "4f": 4, "5d": 5}[a.workload]
     wl = CONFIGS[name]["workload"] + ({"4a": " [int8]", "4b": " [int4]", "4f": " [fp8 e4m3]",
@@ -589,12 +608,16 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(PROFILE_NAME[a.workload] + (f"_window{a.window}" if a.window else "")),
+            # HIP events on the launch stream at the start and end of the
+            # timed region: its K back-to-back steps, launch gaps included
             "kernel_avg_us": round(k_avg * 1e3, 3),
-            "kernel_p10_us": round(float(np.percentile(kern_ms, 10)) * 1e3, 3),
-            "kernel_p90_us": round(float(np.percentile(kern_ms, 90)) * 1e3, 3),
+            "kernel_time": "events around the timed region / steps",
         },
         "input_generation_s": round(gen_s, 2),
     }
+    if a.workload == "2" and not a.window and not a.no_extra:
+        # the other bf16 decode workloads, so one default run times all three
+        res["other_bf16_decode"] = extra_decode_configs(torch, B, a.steps, a.warmup, a.layers)
     if not a.no_read_probe:
         # the same box's measured read ceiling, beside the spec peak
         rc = read_ceiling(torch, B)
