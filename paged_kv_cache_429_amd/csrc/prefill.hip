@@ -501,7 +501,7 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
     // it moves it moves to the row's new maximum, whose own term is then
     // exactly 2^0.
     constexpr float kSlack = 8.f;
-    auto stage = [&](const uint8_t* buf, int kb, auto diag_tag) {
+    auto stage = [&](const uint8_t* buf, int kb, auto diag_tag) __attribute__((always_inline)) {
         constexpr bool DIAG = decltype(diag_tag)::value;
         const uint8_t* kst = buf;
         const uint8_t* vst = buf + kStageBlocks * kTile128;
@@ -581,14 +581,14 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
         __builtin_amdgcn_s_setprio(0);
     };
 
-    prefetch(st_begin, lds + (st_begin & 1) * kStageBytes);
-    commit(st_begin, lds + (st_begin & 1) * kStageBytes);
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's K loads have landed
-    __syncthreads();
-    for (int st = st_begin; st < nstage; ++st) {
+    // One loop step: the next stage's loads go out into the other buffer
+    // (last read before the previous barrier), the wave computes stage st
+    // (FULL: every row of the workgroup sees all of it; else the wave
+    // decides), the staged V of st + 1 is written, and the barrier hands
+    // that buffer over.
+    auto step = [&](int st, auto full_tag) __attribute__((always_inline)) {
         uint8_t* buf = lds + (st & 1) * kStageBytes;
         uint8_t* nbuf = lds + ((st + 1) & 1) * kStageBytes;
-        // the other buffer was last read before the previous barrier
         if (st + 1 < nstage) prefetch(st + 1, nbuf);
         const int kb = st * kStageKeys;
         // Rows of this wave whose position is at least kb + 63 see the whole
@@ -596,7 +596,7 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
         // a window, one holding some row's window start. A stage past every
         // row, or wholly before every row's window, is skipped. (Rows past the
         // chunk end never get stored.)
-        if (PREFIX || (kb + kStageKeys - 1 <= shift + wfirst && kb >= wave_khi)) {
+        if (decltype(full_tag)::value || PREFIX || (kb + kStageKeys - 1 <= shift + wfirst && kb >= wave_khi)) {
             stage(buf, kb, std::false_type{});
         } else if (kb <= wave_kmax && kb + kStageKeys - 1 >= wave_klo) {
             stage(buf, kb, std::true_type{});
@@ -606,7 +606,26 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
             __builtin_amdgcn_s_waitcnt(0);  // this thread's K loads have landed
         }
         __syncthreads();
+    };
+    // stages [full_lo, full_hi) are whole for every row of the workgroup: no
+    // mask and no per-wave choice, so they run in a loop of their own
+    int full_lo = st_begin, full_hi = nstage;
+    if constexpr (!PREFIX) {
+        full_hi = min(nstage, max(st_begin, (shift + i0 + 1) / kStageKeys));
+        if (p.window > 0) {
+            const int khi = shift + min(qlen - 1, i0 + QT - 1) - p.window + 1;  // last row's window start
+            full_lo = max(st_begin, (max(khi, 0) + kStageKeys - 1) / kStageKeys);
+        }
+        if (full_lo > full_hi) full_lo = full_hi;
     }
+
+    prefetch(st_begin, lds + (st_begin & 1) * kStageBytes);
+    commit(st_begin, lds + (st_begin & 1) * kStageBytes);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's K loads have landed
+    __syncthreads();
+    for (int st = st_begin; st < full_lo; ++st) step(st, std::false_type{});
+    for (int st = full_lo; st < full_hi; ++st) step(st, std::true_type{});
+    for (int st = full_hi; st < nstage; ++st) step(st, std::false_type{});
 
     const float lt = l + __shfl_xor(l, 32);
     if (!row_ok) return;
