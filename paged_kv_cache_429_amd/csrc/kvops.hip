@@ -94,34 +94,55 @@ __device__ __forceinline__ int quant_code(float x, float sf, bool zero) {
     }
 }
 
-// BITS 8 or 4 (integer codes) or 0 (fp8 e4m3 codes, one byte each).
+// BITS 8 or 4 (integer codes) or 0 (fp8 e4m3 codes, one byte each). One
+// wave per (block, KV head) tile: the bf16 tile comes in with 16-byte loads
+// (its largest magnitude taken on the way) and is kept in LDS, where each
+// code reads its source element; the codes leave in 16-byte stores.
 template <int D, int BITS, int KIND>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ src, uint8_t* __restrict__ codes,
                                                       uint16_t* __restrict__ scales, const int32_t* __restrict__ ids,
                                                       int n_ids, int num_blocks, int n_kv) {
+    constexpr int N = 16 * D;                       // elements of a tile
+    constexpr int CB = BITS == 0 ? 8 : BITS;        // bits per code
+    constexpr int IN16 = N * 2 / 16;                // 16-byte pieces of the bf16 tile
+    constexpr int OUT16 = N * CB / 8 / 16;          // 16-byte pieces of its codes
+    __shared__ __attribute__((aligned(16))) uint16_t stage[4][N];
     const int lane = threadIdx.x & 63;
-    const long tile = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (tile >= (long)n_ids * n_kv) return;
-    const int i_id = (int)(tile / n_kv);
-    const int h = (int)(tile % n_kv);
-    const int b = ids ? ids[i_id] : i_id;
-    if ((unsigned)b >= (unsigned)num_blocks) return;
-    constexpr int N = 16 * D;
-    const uint16_t* t = src + ((size_t)b * n_kv + h) * N;
-
+    const int w = threadIdx.x >> 6;
+    const long tile = (long)blockIdx.x * 4 + w;
+    int b = -1, h = 0;
+    if (tile < (long)n_ids * n_kv) {
+        const int i_id = (int)(tile / n_kv);
+        h = (int)(tile % n_kv);
+        b = ids ? ids[i_id] : i_id;
+        if ((unsigned)b >= (unsigned)num_blocks) b = -1;
+    }
+    uint16_t* st = stage[w];
     float amax = 0.f;
-    for (int e = lane; e < N; e += 64) amax = fmaxf(amax, fabsf(bf16_bits_to_f32(t[e])));
+    if (b >= 0) {
+        const u32x4* t = reinterpret_cast<const u32x4*>(src + ((size_t)b * n_kv + h) * N);
+        for (int c = lane; c < IN16; c += 64) {
+            const u32x4 v = t[c];
+            *reinterpret_cast<u32x4*>(st + 8 * c) = v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                amax = fmaxf(amax, fabsf(__uint_as_float(v[e] << 16)));
+                amax = fmaxf(amax, fabsf(__uint_as_float(v[e] & 0xffff0000u)));
+            }
+        }
+    }
+    __syncthreads();  // the tile is in LDS
+    if (b < 0) return;
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
 
-    constexpr int CB = BITS == 0 ? 8 : BITS;       // bits per code
     uint16_t sbits;
     bool zero;
     const float sf = tile_scale<BITS>(amax, &sbits, &zero);
     if (lane == 0) scales[(size_t)b * n_kv + h] = sbits;
 
-    auto code_of = [&](int n) -> int {
-        // element n of the int tile -> (slot, dim) -> source element
+    auto code_of = [&](int n) -> uint32_t {
+        // element n of the code tile -> (slot, dim) -> element of the bf16 tile
         int tt, ii;
         if (KIND == 0) {
             constexpr int x = 128 / CB;
@@ -132,18 +153,25 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
             v_elem<D, CB>(n, tt, ii);
         }
         const int se = (KIND == 0) ? k_elem(tt, ii, 8) : ii * 16 + tt;
-        return quant_code<BITS>(bf16_bits_to_f32(t[se]), sf, zero);
+        return (uint32_t)quant_code<BITS>(bf16_bits_to_f32(st[se]), sf, zero);
     };
 
-    uint8_t* out = codes + ((size_t)b * n_kv + h) * (N * CB / 8);
-    for (int o = lane; o < N * CB / 8; o += 64) {
-        if (CB == 8) {
-            out[o] = (uint8_t)code_of(o);
-        } else {
-            const int lo = code_of(2 * o) & 0xf;
-            const int hi = code_of(2 * o + 1) & 0xf;
-            out[o] = (uint8_t)(lo | (hi << 4));
+    u32x4* out = reinterpret_cast<u32x4*>(codes + ((size_t)b * n_kv + h) * (N * CB / 8));
+    for (int c = lane; c < OUT16; c += 64) {
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uint32_t word = 0;
+            if (CB == 8) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) word |= (code_of(16 * c + 4 * e + k) & 0xffu) << (8 * k);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) word |= (code_of(32 * c + 8 * e + k) & 0xfu) << (4 * k);
+            }
+            o[e] = word;
         }
+        out[c] = o;
     }
 }
 
