@@ -130,10 +130,13 @@ struct Mfma {
     // in fp32.
     static constexpr bool kOffset = (FMT == FMT_I4 || FMT == FMT_I8);
     static constexpr float kOff = (FMT == FMT_I4) ? 136.f : 128.f;
+    // int4 decode operands come with each group of eight k in the order
+    // 0, 2, 4, 6, 1, 3, 5, 7 (i4x8_to_bf16x8_off136_eo); Q and P follow it
+    static constexpr bool kEvenOdd = (FMT == FMT_I4);
 
     __device__ static __forceinline__ u32x4 k_operand_dec(const KRaw& r, int kk) {
         if constexpr (FMT == FMT_I4) {
-            return i4x8_to_bf16x8_off136(r.w[kk]);
+            return i4x8_to_bf16x8_off136_eo(r.w[kk]);
         } else if constexpr (FMT == FMT_I8) {
             const u32x2 lo = i8x4_to_bf16x4_off128(r.w[2 * kk]);
             const u32x2 hi = i8x4_to_bf16x4_off128(r.w[2 * kk + 1]);
@@ -255,7 +258,7 @@ struct Mfma {
             a[2] = hi[0];
             a[3] = hi[1];
         } else {
-            a = i4x8_to_bf16x8_off136(r.w[nb]);  // offset by kOff (see k_operand_dec)
+            a = i4x8_to_bf16x8_off136_eo(r.w[nb]);  // offset by kOff, even-odd order (see k_operand_dec)
         }
         return a;
     }
@@ -393,10 +396,10 @@ __device__ __forceinline__ void softmax_update(ColState<D>& c, const float* x, f
 // block q / 2 (the V operand is then one contiguous run of a V tile row).
 // The probabilities arrive in the S^T layout (lane group q: tokens
 // 4q..4q+3 of each block); two cross-row swaps regroup them within each
-// column. t0 is the pair's first token; V slots at or past ctx (and a
-// missing second block) are zeroed, since their contents may be anything
-// (0 * NaN = NaN). Columns with own == false contribute a zero P column
-// (their accumulator is unchanged).
+// column. t0 is the pair's first token; bf16 and fp8 V slots at or past ctx
+// (and a missing second block) are zeroed, since their contents may be
+// anything (0 * NaN = NaN). Columns with own == false contribute a zero P
+// column (their accumulator is unchanged).
 template <int D, int FMT>
 __device__ __forceinline__ void pv_update(ColState<D>& c, const VHalf<D, FMT>& r, const float* pr, int t0, int ctx,
                                           bool has1, bool own) {
@@ -426,10 +429,14 @@ __device__ __forceinline__ void pv_update(ColState<D>& c, const VHalf<D, FMT>& r
     };
     regroup(a0, b0);
     regroup(a1, b1);
-    const u32x4 pop = {a0, a1, b0, b1};
+    u32x4 pop = {a0, a1, b0, b1};
+    if constexpr (M::kEvenOdd) pop = bf16x8_even_odd(pop);
     const int blk = q >> 1;
     const int tok = t0 + kBlock * blk + 8 * (q & 1);  // first token of this lane group's run
-    const bool tail = !has1 || t0 + 2 * kBlock > ctx;
+    // Integer codes (the offset formats) are finite whatever the pool holds,
+    // and the P of a token at or past ctx is exactly 0, so only bf16 and fp8
+    // tiles, whose bytes may hold NaN, need the V mask.
+    const bool tail = !M::kOffset && (!has1 || t0 + 2 * kBlock > ctx);
     uint32_t msk[4] = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
     if (tail) {
         const bool blk_ok = blk == 0 || has1;
@@ -441,10 +448,12 @@ __device__ __forceinline__ void pv_update(ColState<D>& c, const VHalf<D, FMT>& r
 #pragma unroll
     for (int nb = 0; nb < M::NB; ++nb) {
         u32x4 vop = M::v_pair_op(r.v, nb);
-        vop[0] &= msk[0];
-        vop[1] &= msk[1];
-        vop[2] &= msk[2];
-        vop[3] &= msk[3];
+        if constexpr (!M::kOffset) {
+            vop[0] &= msk[0];
+            vop[1] &= msk[1];
+            vop[2] &= msk[2];
+            vop[3] &= msk[3];
+        }
         c.acc[nb] = mfma_16x16x32(vop, pop, c.acc[nb]);
     }
 }
@@ -538,6 +547,7 @@ __device__ __forceinline__ void load_qop(const DecodeParams& p, int s, int qh, b
 #pragma unroll
     for (int kk = 0; kk < M::KSTEPS; ++kk) {
         qop[kk] = used ? *reinterpret_cast<const u32x4*>(qrow + M::dbase(kk, q)) : u32x4{0u, 0u, 0u, 0u};
+        if constexpr (M::kEvenOdd) qop[kk] = bf16x8_even_odd(qop[kk]);
     }
 }
 

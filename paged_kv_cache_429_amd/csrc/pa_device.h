@@ -164,6 +164,35 @@ __device__ __forceinline__ u32x4 i4x8_to_bf16x8_off136(uint32_t w) {
     return r;
 }
 
+// The same values as i4x8_to_bf16x8_off136, elements in the order
+// 0, 2, 4, 6, 1, 3, 5, 7 (dword j holds elements 2j, 2j + 2 for j < 2 and
+// 2j - 3, 2j - 1 for j >= 2): each dword is one v_perm of the even or odd
+// nibbles with bf16 128's high byte taken from a constant, so no OR is
+// needed. The other MFMA operand takes the same order (bf16x8_even_odd).
+__device__ __forceinline__ u32x4 i4x8_to_bf16x8_off136_eo(uint32_t w) {
+    const uint32_t x = w ^ 0x88888888u;
+    const uint32_t a = x & 0x0f0f0f0fu;         // byte k: element 2k + 8
+    const uint32_t b = (x >> 4) & 0x0f0f0f0fu;  // byte k: element 2k + 1 + 8
+    const uint32_t hi = 0x43434343u;
+    u32x4 r;
+    r[0] = __builtin_amdgcn_perm(hi, a, 0x04010400u);  // elements 0, 2
+    r[1] = __builtin_amdgcn_perm(hi, a, 0x04030402u);  // elements 4, 6
+    r[2] = __builtin_amdgcn_perm(hi, b, 0x04010400u);  // elements 1, 3
+    r[3] = __builtin_amdgcn_perm(hi, b, 0x04030402u);  // elements 5, 7
+    return r;
+}
+
+// Eight 16-bit values (dword j = elements 2j, 2j + 1) reordered to
+// 0, 2, 4, 6, 1, 3, 5, 7, the order of i4x8_to_bf16x8_off136_eo.
+__device__ __forceinline__ u32x4 bf16x8_even_odd(u32x4 v) {
+    u32x4 r;
+    r[0] = __builtin_amdgcn_perm(v[1], v[0], 0x05040100u);
+    r[1] = __builtin_amdgcn_perm(v[3], v[2], 0x05040100u);
+    r[2] = __builtin_amdgcn_perm(v[1], v[0], 0x07060302u);
+    r[3] = __builtin_amdgcn_perm(v[3], v[2], 0x07060302u);
+    return r;
+}
+
 // Exact int4 -> bf16 of the four nibbles in the low 16 bits.
 __device__ __forceinline__ u32x2 i4x4_to_bf16x4(uint32_t w) {
     u32x4 t = i4x8_to_bf16x8(w);
