@@ -130,6 +130,7 @@ struct Mfma {
     // in fp32.
     static constexpr bool kOffset = (FMT == FMT_I4 || FMT == FMT_I8);
     static constexpr float kOff = (FMT == FMT_I4) ? 136.f : 128.f;
+    static constexpr uint32_t kOffBf16 = (FMT == FMT_I4) ? 0x4308u : 0x4300u;  // kOff as bf16
     // int4 decode operands come with each group of eight k in the order
     // 0, 2, 4, 6, 1, 3, 5, 7 (i4x8_to_bf16x8_off136_eo); Q and P follow it
     static constexpr bool kEvenOdd = (FMT == FMT_I4);
@@ -303,14 +304,16 @@ template <int D>
 struct ColState {
     float m, l;
     f32x4 acc[D / 16];
-    float corr;  // offset formats: this lane's share of kOff * sum(P), rescaled with acc
+    // offset formats: kOff * sum(P) of the lane's column (every element; an
+    // MFMA of a constant kOff operand with the P operands), rescaled with acc
+    f32x4 corr;
 };
 
 template <int D>
 __device__ __forceinline__ void col_init(ColState<D>& c) {
     c.m = kNegInf;
     c.l = 0.f;
-    c.corr = 0.f;
+    c.corr = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) c.acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
@@ -382,12 +385,12 @@ __device__ __forceinline__ void softmax_update(ColState<D>& c, const float* x, f
         psum += pr[i];
     }
     c.l = c.l * alpha + psum;
-    c.corr *= alpha;
     // alpha is exactly 1 in every column of the wave unless some maximum
     // moved; multiplying by 1 changes nothing, so that common case skips it
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
         for (int nb = 0; nb < D / 16; ++nb) c.acc[nb] *= alpha;
+        c.corr *= alpha;
     }
 }
 
@@ -411,12 +414,6 @@ __device__ __forceinline__ void pv_update(ColState<D>& c, const VHalf<D, FMT>& r
     uint32_t b0 = pack_bf16x2(pr[4] * r.s1, pr[5] * r.s1);
     uint32_t b1 = pack_bf16x2(pr[6] * r.s1, pr[7] * r.s1);
     if (!own) a0 = a1 = b0 = b1 = 0u;
-    if constexpr (M::kOffset) {  // kOff * the P values exactly as the MFMA sees them
-        auto lo = [](uint32_t x) { return __uint_as_float(x << 16); };
-        auto hi = [](uint32_t x) { return __uint_as_float(x & 0xffff0000u); };
-        const float ps = ((lo(a0) + hi(a0)) + (lo(a1) + hi(a1))) + ((lo(b0) + hi(b0)) + (lo(b1) + hi(b1)));
-        c.corr += M::kOff * ps;
-    }
     // Rows (lane groups) 0..3 of a = a@0..a@3, likewise b. After the 32-lane
     // swap a = [a@0 a@1 b@0 b@1], b = [a@2 a@3 b@2 b@3]; after the 16-lane
     // swap a = [a@0 a@2 b@0 b@2] (first four tokens of the group's run) and
@@ -445,6 +442,10 @@ __device__ __forceinline__ void pv_update(ColState<D>& c, const VHalf<D, FMT>& r
             msk[w] = (blk_ok && tok + 2 * w < ctx ? 0x0000ffffu : 0u) | (blk_ok && tok + 2 * w + 1 < ctx ? 0xffff0000u : 0u);
         }
     }
+    if constexpr (M::kOffset) {  // kOff * the P values exactly as the MFMA sees them
+        const uint32_t k2 = M::kOffBf16 * 0x10001u;
+        c.corr = mfma_16x16x32(u32x4{k2, k2, k2, k2}, pop, c.corr);
+    }
 #pragma unroll
     for (int nb = 0; nb < M::NB; ++nb) {
         u32x4 vop = M::v_pair_op(r.v, nb);
@@ -469,11 +470,8 @@ __device__ __forceinline__ void col_to_lds(ColState<D>& c, WaveState<D>& st, int
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     if constexpr (OFFSET) {  // remove the operand offset's share of the accumulator
-        float corr = c.corr;
-        corr += __shfl_xor(corr, 16);
-        corr += __shfl_xor(corr, 32);
 #pragma unroll
-        for (int nb = 0; nb < D / 16; ++nb) c.acc[nb] -= corr;
+        for (int nb = 0; nb < D / 16; ++nb) c.acc[nb] -= c.corr[0];
     }
     if (q == 0) {
         st.m[wave][g] = c.m;

@@ -170,9 +170,9 @@ __device__ __forceinline__ u32x4 i4x8_to_bf16x8_off136(uint32_t w) {
 // nibbles with bf16 128's high byte taken from a constant, so no OR is
 // needed. The other MFMA operand takes the same order (bf16x8_even_odd).
 __device__ __forceinline__ u32x4 i4x8_to_bf16x8_off136_eo(uint32_t w) {
-    const uint32_t x = w ^ 0x88888888u;
-    const uint32_t a = x & 0x0f0f0f0fu;         // byte k: element 2k + 8
-    const uint32_t b = (x >> 4) & 0x0f0f0f0fu;  // byte k: element 2k + 1 + 8
+    // each a three-input bitwise op (v_bitop3) of w or w >> 4
+    const uint32_t a = (w ^ 0x88888888u) & 0x0f0f0f0fu;         // byte k: element 2k + 8
+    const uint32_t b = ((w >> 4) ^ 0x08080808u) & 0x0f0f0f0fu;  // byte k: element 2k + 1 + 8
     const uint32_t hi = 0x43434343u;
     u32x4 r;
     r[0] = __builtin_amdgcn_perm(hi, a, 0x04010400u);  // elements 0, 2
