@@ -199,43 +199,120 @@ hipError_t launch_quantize(const void* src, void* codes, uint16_t* scales, const
     return hipErrorInvalidValue;
 }
 
-// One thread per (token, KV head, 16-byte chunk of the source row).
+// Scatter of source rows to arbitrary slots. One wave per 64 source tokens
+// and one KV head. A token is a run head when its slot is the first of a
+// block and the next 15 tokens hold that block's next 15 slots in order
+// (rows written in order, as a prompt's are): the head's wave writes the
+// block's whole K and V tiles with 16-byte stores, K chunk by chunk and V
+// transposed through LDS. The 15 tokens after a head are left to it. Every
+// other token in range is written by the whole wave: its K row as 16-byte
+// chunks, its V row element by element (a V tile is dim-major, so one
+// token's elements are 16 slots apart).
 template <int D, int EB>
 __global__ __launch_bounds__(256) void kv_write_kernel(const uint8_t* __restrict__ ksrc,
                                                       const uint8_t* __restrict__ vsrc,
                                                       const int64_t* __restrict__ slots, int ntok,
                                                       uint8_t* __restrict__ kpool, uint8_t* __restrict__ vpool,
                                                       int num_blocks, int n_kv) {
-    constexpr int CH = D * EB / 16;   // chunks per row
-    constexpr int X = 16 / EB;        // elements per chunk
-    constexpr size_t TILE = (size_t)16 * D * EB;
-    const long gid = (long)blockIdx.x * 256 + threadIdx.x;
-    const long total = (long)ntok * n_kv * CH;
-    if (gid >= total) return;
-    const int c = (int)(gid % CH);
-    const int h = (int)((gid / CH) % n_kv);
-    const long tok = gid / ((long)CH * n_kv);
-    const int64_t slot = slots[tok];
-    if (slot < 0 || slot >= (int64_t)num_blocks * 16) return;
-    const int64_t b = slot / 16;
-    const int t = (int)(slot % 16);
-    const size_t tile = ((size_t)b * n_kv + h) * TILE;
-    const size_t src = ((size_t)tok * n_kv + h) * D * EB + (size_t)c * 16;
-    if (ksrc) {
-        *reinterpret_cast<u32x4*>(kpool + tile + (size_t)(c * 16 + t) * 16) =
-            *reinterpret_cast<const u32x4*>(ksrc + src);
+    constexpr int ROW = D * EB;        // bytes of one token's row of one head
+    constexpr int CH = ROW / 16;       // its 16-byte chunks
+    constexpr int TILE = 16 * ROW;     // bytes of a (block, head) tile
+    constexpr int PER = 16 / EB;       // elements per 16-byte piece
+    constexpr int PIECES = TILE / 16;  // 16-byte pieces of a tile
+    __shared__ __attribute__((aligned(16))) uint8_t stage[4][TILE];
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const long t0 = ((long)blockIdx.x * 4 + w) * 64;
+    const int h = blockIdx.y;
+    if (t0 >= ntok) return;  // (no workgroup barrier below)
+    const int64_t nslots = (int64_t)num_blocks * 16;
+    auto slot_of = [&](long t) -> int64_t {  // -1: no token, or a slot that is skipped
+        if (t < 0 || t >= ntok) return -1;
+        const int64_t s = slots[t];
+        return (s >= 0 && s < nslots) ? s : -1;
+    };
+    auto is_head = [&](long t) -> bool {
+        const int64_t s = slot_of(t);
+        if (s < 0 || (s & 15) != 0) return false;
+        for (int j = 1; j < 16; ++j) {
+            if (slot_of(t + j) != s + j) return false;
+        }
+        return true;
+    };
+    const int64_t s_me = slot_of(t0 + lane);
+    const uint64_t heads = __builtin_amdgcn_ballot_w64(is_head(t0 + lane));              // bit l: token t0 + l
+    const uint64_t prev = __builtin_amdgcn_ballot_w64(lane < 15 && is_head(t0 - 15 + lane));  // bit l: t0 - 15 + l
+    bool covered = false;  // a head lies 1..15 tokens before this lane's token
+    for (int j = 1; j < 16; ++j) {
+        const int d = lane - j;
+        covered = covered || (d >= 0 ? ((heads >> d) & 1) : ((prev >> (d + 15)) & 1));
     }
-    if (vsrc) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(vsrc + src);
-        const uint8_t* vb = reinterpret_cast<const uint8_t*>(&v);
+    auto shfl_slot = [&](int l) -> int64_t {
+        const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)s_me, l);
+        const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)((uint64_t)s_me >> 32), l);
+        return (int64_t)(((uint64_t)hi << 32) | lo);
+    };
+    auto src_row = [&](const uint8_t* src, long t) { return src + ((size_t)t * n_kv + h) * ROW; };
+
+    for (uint64_t hm = heads; hm; hm &= hm - 1) {  // whole tiles
+        const int l = __builtin_ctzll(hm);
+        const long th = t0 + l;
+        const size_t tile = ((size_t)(shfl_slot(l) / 16) * n_kv + h) * TILE;
+        if (ksrc) {  // tile chunk c of slot t is chunk c of row th + t
+            for (int j = lane; j < 16 * CH; j += 64) {
+                *reinterpret_cast<u32x4*>(kpool + tile + (size_t)j * 16) =
+                    *reinterpret_cast<const u32x4*>(src_row(ksrc, th + j % 16) + (j / 16) * 16);
+            }
+        }
+        if (vsrc) {
+            uint8_t* st = stage[w];
+            for (int j = lane; j < 16 * CH; j += 64) {  // row t at st + t * ROW
+                *reinterpret_cast<u32x4*>(st + (j / CH) * ROW + (j % CH) * 16) =
+                    *reinterpret_cast<const u32x4*>(src_row(vsrc, th + j / CH) + (j % CH) * 16);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_wave_barrier();
+            for (int q = lane; q < PIECES; q += 64) {  // piece q: dim q / (16 / PER), slots from tf on
+                const int i = q / (16 / PER);
+                const int tf = (q % (16 / PER)) * PER;
+                u32x4 o;
 #pragma unroll
-        for (int e = 0; e < X; ++e) {
-            const int i = c * X + e;
-            uint8_t* dst = vpool + tile + (size_t)(i * 16 + t) * EB;
-            if (EB == 2) {
-                *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(vb + 2 * e);
-            } else {
-                *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(vb + 4 * e);
+                for (int e = 0; e < 4; ++e) {
+                    if (EB == 2) {
+                        const uint32_t lo = *reinterpret_cast<const uint16_t*>(st + (tf + 2 * e) * ROW + i * 2);
+                        const uint32_t hi = *reinterpret_cast<const uint16_t*>(st + (tf + 2 * e + 1) * ROW + i * 2);
+                        o[e] = lo | (hi << 16);
+                    } else {
+                        o[e] = *reinterpret_cast<const uint32_t*>(st + (tf + e) * ROW + i * 4);
+                    }
+                }
+                *reinterpret_cast<u32x4*>(vpool + tile + (size_t)q * 16) = o;
+            }
+            __builtin_amdgcn_s_waitcnt(0);  // the stage is read before the next head overwrites it
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+
+    const bool single = s_me >= 0 && !((heads >> lane) & 1) && !covered;
+    for (uint64_t sm = __builtin_amdgcn_ballot_w64(single); sm; sm &= sm - 1) {  // tokens on their own
+        const int l = __builtin_ctzll(sm);
+        const int64_t s = shfl_slot(l);
+        const int t = (int)(s % 16);
+        const size_t tile = ((size_t)(s / 16) * n_kv + h) * TILE;
+        if (ksrc) {
+            for (int c = lane; c < CH; c += 64) {
+                *reinterpret_cast<u32x4*>(kpool + tile + (size_t)(c * 16 + t) * 16) =
+                    *reinterpret_cast<const u32x4*>(src_row(ksrc, t0 + l) + c * 16);
+            }
+        }
+        if (vsrc) {
+            for (int i = lane; i < D; i += 64) {
+                uint8_t* dst = vpool + tile + (size_t)(i * 16 + t) * EB;
+                if (EB == 2) {
+                    *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(src_row(vsrc, t0 + l) + i * 2);
+                } else {
+                    *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src_row(vsrc, t0 + l) + i * 4);
+                }
             }
         }
     }
@@ -244,11 +321,10 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const uint8_t* __restrict
 template <int D, int EB>
 static hipError_t write_t(const void* k_src, const void* v_src, const int64_t* slots, int ntok, void* kp, void* vp,
                           int num_blocks, int n_kv, hipStream_t stream) {
-    const long total = (long)ntok * n_kv * (D * EB / 16);
-    if (total == 0) return hipSuccess;
-    const long grid = (total + 255) / 256;
-    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((kv_write_kernel<D, EB>), dim3((unsigned)grid), dim3(256), 0, stream,
+    if (ntok == 0 || n_kv == 0) return hipSuccess;
+    const long grid = ((long)ntok + 255) / 256;
+    if (grid > 0x7fffffffL || n_kv > 65535) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((kv_write_kernel<D, EB>), dim3((unsigned)grid, (unsigned)n_kv), dim3(256), 0, stream,
                        static_cast<const uint8_t*>(k_src), static_cast<const uint8_t*>(v_src), slots, ntok,
                        static_cast<uint8_t*>(kp), static_cast<uint8_t*>(vp), num_blocks, n_kv);
     return hipGetLastError();

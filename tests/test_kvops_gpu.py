@@ -47,6 +47,67 @@ def test_kv_write_partial_and_skipped_slots(lib):
     assert not np.array_equal(_img(kp), before_k)
 
 
+def _mixed_slot_mapping(num_blocks, seed):
+    """A slot list mixing whole blocks written in order (some starting just
+    before a multiple of 64 source rows, so that the block's tokens span two
+    groups of 64), a block with one slot out of place, a block written in
+    reverse, a partly written block, scattered single slots, and skipped
+    (negative, out-of-range) entries. Every slot appears at most once."""
+    g = np.random.default_rng(seed)
+    blocks = iter(g.permutation(num_blocks).tolist())
+    out = []
+
+    def block_run(n=16):  # the first n slots of a fresh block, in order
+        b = next(blocks)
+        return [b * 16 + j for j in range(n)]
+
+    def pad_to(n):  # single slots, every other slot of fresh blocks, until len(out) == n
+        while len(out) < n:
+            out.extend(block_run()[::2][: n - len(out)])
+    out += block_run()                      # run at row 0
+    pad_to(49)
+    out += block_run()                      # run at rows 49..64
+    out += [-1, num_blocks * 16 + 3]        # skipped
+    pad_to(127)
+    out += block_run()                      # head at row 127, the last row of a group of 64
+    run = block_run()
+    run[7] = next(blocks) * 16 + 2          # one slot out of place: no run
+    out += run
+    out += block_run()[::-1]                # reversed
+    out += block_run(10)                    # partly written block
+    for _ in range(5):
+        out += block_run()                  # plain runs
+    out.append(next(blocks) * 16 + 5)       # a last single slot
+    return np.array(out, dtype=np.int64)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
+def test_kv_write_runs_and_scattered_slots(lib, dtype, d):
+    """Whole-block runs (written as tiles) and tokens written one by one in
+    the same call land exactly where the slot list says; every other byte of
+    the pools is untouched."""
+    c = make_decode_case(8, 2, d, dtype, [40], 403 + d, pool_blocks=64)
+    kp, vp = upload_pools(c)
+    slots = _mixed_slot_mapping(c.num_blocks, 404 + d)
+    n = len(slots)
+    g = np.random.default_rng(405 + d)
+    if dtype == "f32":
+        newk = g.standard_normal((n, 2, d)).astype(np.float32)
+        newv = g.standard_normal((n, 2, d)).astype(np.float32)
+    else:
+        newk = g.integers(0, 1 << 15, size=(n, 2, d)).astype(np.uint16)
+        newv = g.integers(0, 1 << 15, size=(n, 2, d)).astype(np.uint16)
+    B.kv_write(np_to_dev(newk, dtype), np_to_dev(newv, dtype), torch.from_numpy(slots).cuda(), kp, vp, n_kv_heads=2)
+    torch.cuda.synchronize()
+    ks, vs = c.k_slots.copy(), c.v_slots.copy()
+    for i, sl in enumerate(slots):
+        if 0 <= sl < c.num_blocks * 16:
+            ks[sl], vs[sl] = newk[i], newv[i]
+    bits = 32 if dtype == "f32" else 16
+    assert np.array_equal(_img(kp), pack_pool(ks, "k", bits))
+    assert np.array_equal(_img(vp), pack_pool(vs, "v", bits))
+
+
 @pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("kind", ["k", "v"])
 @pytest.mark.parametrize("d", [64, 128])
