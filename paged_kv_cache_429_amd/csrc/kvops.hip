@@ -80,14 +80,25 @@ __device__ __forceinline__ float tile_scale(float amax, uint16_t* bits, bool* ze
 
 // Code of x under the tile scale sf: clamp(rint(x / sf), -qmax, qmax) for
 // integer codes, the e4m3 code nearest x / sf for fp8 (BITS 0); 0 if zero.
+// x / sf is the correctly rounded float quotient. For integer codes rsf (a
+// reciprocal of sf, within one ulp) stands in for the division: for
+// |x * rsf| < 128 the product is within 2^-14.6 of x / sf, so when it lies
+// more than 2^-12 from every half-integer both round to the same integer;
+// otherwise (and for a non-finite product) the quotient itself is taken.
 template <int BITS>
-__device__ __forceinline__ int quant_code(float x, float sf, bool zero) {
+__device__ __forceinline__ int quant_code(float x, float sf, float rsf, bool zero) {
     if (zero) return 0;
-    const float r = x / sf;
     if constexpr (BITS == 0) {
-        return (int)f32_to_e4m3(r);
+        return (int)f32_to_e4m3(x / sf);
     } else {
         constexpr float qmax = (BITS == 8) ? 127.f : 7.f;
+        float r = x * rsf;
+        const float h = fabsf(r - __builtin_floorf(r) - 0.5f);  // distance to the nearest half-integer
+        const bool exact = !(h > 0x1p-12f && fabsf(r) < 128.f);
+        if (__builtin_amdgcn_ballot_w64(exact)) {  // rare: the division only where some lane needs it
+            const float q = x / sf;
+            r = exact ? q : r;
+        }
         float c = __builtin_rintf(r);
         c = fminf(fmaxf(c, -qmax), qmax);
         return (int)c;
@@ -139,6 +150,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     uint16_t sbits;
     bool zero;
     const float sf = tile_scale<BITS>(amax, &sbits, &zero);
+    const float rsf = __builtin_amdgcn_rcpf(sf);
     if (lane == 0) scales[(size_t)b * n_kv + h] = sbits;
 
     auto code_of = [&](int n) -> uint32_t {
@@ -153,7 +165,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
             v_elem<D, CB>(n, tt, ii);
         }
         const int se = (KIND == 0) ? k_elem(tt, ii, 8) : ii * 16 + tt;
-        return (uint32_t)quant_code<BITS>(bf16_bits_to_f32(st[se]), sf, zero);
+        return (uint32_t)quant_code<BITS>(bf16_bits_to_f32(st[se]), sf, rsf, zero);
     };
 
     u32x4* out = reinterpret_cast<u32x4*>(codes + ((size_t)b * n_kv + h) * (N * CB / 8));
@@ -493,6 +505,7 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AppendParams p) {
         uint16_t sbits;
         bool zero;
         const float sf = tile_scale<BITS>(amax, &sbits, &zero);
+        const float rsf = __builtin_amdgcn_rcpf(sf);
         if (lane == 0) p.scales[kind][(size_t)phys * p.n_kv + kvh] = sbits;
         for (int k = lane; k < TILE / 16; k += 64) {
             u32x4 w = {0u, 0u, 0u, 0u};
@@ -500,7 +513,7 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AppendParams p) {
             for (int e = 0; e < EPC; ++e) {
                 int t, i;
                 elem(k * EPC + e, t, i);
-                const uint32_t c = (uint32_t)quant_code<BITS>(tile[t][i], sf, zero) & ((1u << CB) - 1u);
+                const uint32_t c = (uint32_t)quant_code<BITS>(tile[t][i], sf, rsf, zero) & ((1u << CB) - 1u);
                 w[(e * CB) / 32] |= c << ((e * CB) % 32);
             }
             *reinterpret_cast<u32x4*>(out + (size_t)k * 16) = w;

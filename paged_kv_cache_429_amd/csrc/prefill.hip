@@ -269,7 +269,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p, int 
 // per (sequence, KV head, tile of 256/G chunk tokens); wave w owns 32 query
 // rows (32/G tokens x G heads), one 32-column MFMA tile, so every MFMA is
 // 32x32x16 with all columns in use, and two waves share each SIMD (one
-// wave's softmax overlaps the other's MFMAs). Keys stream through LDS in
+// wave issues while the other waits on LDS; a SIMD overlaps one wave's
+// MFMAs with another's VALU work only a little, so the stage costs about
+// the sum of the two). Keys stream through LDS in
 // stages of 64 (four blocks of K, then four of V, 32 KiB), double-buffered:
 // the next stage's loads are in flight while this stage is computed, and
 // one barrier per stage hands the buffer over. Per stage and wave:
@@ -506,9 +508,6 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
         const uint8_t* kst = buf;
         const uint8_t* vst = buf + kStageBlocks * kTile128;
         f32x16 sc[2];
-        // MFMA issue at raised wave priority: the two waves of a SIMD drift
-        // apart, so one's softmax overlaps the other's MFMAs
-        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             sc[kt] = f32x16{};
@@ -519,7 +518,6 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
                 sc[kt] = mfma_32x32x16(a, qop[kk], sc[kt]);
             }
         }
-        __builtin_amdgcn_s_setprio(0);
         // scores in log2 units, -inf past the row's position on a diagonal stage
         float mx = kNegInf;
 #pragma unroll
@@ -564,7 +562,6 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
         }
-        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
             const int d = 32 * dt + n;
@@ -578,7 +575,6 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
                 }
             }
         }
-        __builtin_amdgcn_s_setprio(0);
     };
 
     // One loop step: the next stage's loads go out into the other buffer

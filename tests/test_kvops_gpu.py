@@ -126,6 +126,43 @@ def test_quantize_bitexact(lib, bits, kind, d):
     assert np.array_equal(_img(codes), pack_pool(ref_codes, kind, bits))
 
 
+def _tie_tiles(bits, d, n_kv=2, seed=406):
+    """bf16 slot-form tiles whose quotients x / s land exactly on half-integers
+    and one bf16 step either side: each tile's largest magnitude is qmax / 8,
+    so its fp16 scale is exactly 1/8, and x = (k + 1/2) / 8 is a tie."""
+    qmax = 127 if bits == 8 else 7
+    g = np.random.default_rng(seed)
+    nb = 6
+    x = np.zeros((nb * 16, n_kv, d), dtype=np.float32)
+    ties = (np.arange(-qmax, qmax) + 0.5) / 8.0
+    for b in range(nb):
+        for h in range(n_kv):
+            vals = g.choice(ties, size=16 * d)
+            step = b % 3  # 0: exact ties; 1: one bf16 step up; 2: one step down
+            bits16 = (vals.astype(np.float32).view(np.uint32) >> 16).astype(np.int64)
+            bits16 = bits16 + (0 if step == 0 else (1 if step == 1 else -1)) * np.sign(vals).astype(np.int64)
+            vals = (bits16.astype(np.uint32) << 16).view(np.float32)
+            vals[0] = qmax / 8.0 * (1 if b % 2 else -1)  # the tile's largest magnitude
+            x[b * 16:(b + 1) * 16, h, :] = vals.reshape(16, d)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("kind", ["k", "v"])
+def test_quantize_ties_bitexact(lib, bits, kind):
+    """Quotients exactly on half-integers round to even, and one bf16 step
+    either side to the nearest integer, as the oracle's float32 division."""
+    d = 128
+    slots = _tie_tiles(bits, d)
+    src = np_to_dev(np.ascontiguousarray(pack_pool(slots, kind, 16).view(np.uint16)), "bf16")
+    codes, scales = B.quantize(src, bits=bits, kind=0 if kind == "k" else 1, n_kv_heads=2, d_head=d)
+    torch.cuda.synchronize()
+    ref_codes, ref_scales = oracle.quantize_tiles(bf16_bits_to_f32(slots), bits)
+    assert (ref_scales.astype(np.float32) == 0.125).all()
+    assert np.array_equal(scales.cpu().numpy().view(np.uint16), ref_scales.view(np.uint16))
+    assert np.array_equal(unpack_pool(_img(codes), kind, bits, d), ref_codes)
+
+
 def test_quantize_block_subset_and_special_tiles(lib):
     c = make_decode_case(4, 2, 64, "bf16", [64], 403, pool_factor=3.0)
     # tile of zeros and a tile whose fp16 scale overflows
