@@ -16,6 +16,8 @@
 // them) follow the pool layout: K tiles in 16-byte chunks of consecutive dims
 // (slot-minor), V tiles transposed (dim-major).
 #include "pa_device.h"
+
+#include <type_traits>
 #include "pa_internal.h"
 
 namespace pa {
@@ -390,7 +392,17 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AppendParams p) {
     constexpr int BITS = FMT == FMT_F8 ? 0 : CB;           // quant_code selector
     constexpr int TILE = 16 * D * CB / 8;                  // pool bytes of one tile
     constexpr int EPC = 128 / CB;                          // elements per 16-byte pool chunk
-    __shared__ float tile[16][D + 1];
+    // the tile's values: float32 for plain pools, bf16 bits for quantized
+    // ones (whose values are all bf16), which halves the LDS of a workgroup
+    using TileT = std::conditional_t<QUANT, uint16_t, float>;
+    __shared__ TileT tile[16][D + (QUANT ? 2 : 1)];
+    auto tv = [&](int t, int i) -> float {
+        if constexpr (QUANT) {
+            return bf16_bits_to_f32(tile[t][i]);
+        } else {
+            return tile[t][i];
+        }
+    };
 
     const int lane = threadIdx.x;
     const int kind = blockIdx.x & 1;
@@ -440,7 +452,13 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AppendParams p) {
             for (int e = 0; e < SPP; ++e) v[e] = 0.f;
         }
 #pragma unroll
-        for (int e = 0; e < SPP; ++e) tile[t][i0 + e] = v[e];
+        for (int e = 0; e < SPP; ++e) {
+            if constexpr (QUANT) {
+                tile[t][i0 + e] = (uint16_t)(__float_as_uint(v[e]) >> 16);  // a bf16 value: exact
+            } else {
+                tile[t][i0 + e] = v[e];
+            }
+        }
     }
     __syncthreads();
 
@@ -472,7 +490,7 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AppendParams p) {
                 for (int e = 0; e < EPC; ++e) {
                     int t, i;
                     elem(k * EPC + e, t, i);
-                    const float x = tile[t][i];
+                    const float x = tv(t, i);
                     if (SEB == 4) {
                         w[e] = __float_as_uint(x);
                     } else if (e % 2 == 0) {
@@ -488,7 +506,7 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AppendParams p) {
                     int t, i;
                     elem(k * EPC + e, t, i);
                     if (t < lo || t >= hi) continue;
-                    const float x = tile[t][i];
+                    const float x = tv(t, i);
                     if (SEB == 4) {
                         reinterpret_cast<uint32_t*>(out)[k * EPC + e] = __float_as_uint(x);
                     } else {
@@ -499,7 +517,7 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AppendParams p) {
         }
     } else {
         float amax = 0.f;
-        for (int e = lane; e < kBlock * D; e += 64) amax = fmaxf(amax, fabsf(tile[e / D][e % D]));
+        for (int e = lane; e < kBlock * D; e += 64) amax = fmaxf(amax, fabsf(tv(e / D, e % D)));
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
         uint16_t sbits;
@@ -513,7 +531,7 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AppendParams p) {
             for (int e = 0; e < EPC; ++e) {
                 int t, i;
                 elem(k * EPC + e, t, i);
-                const uint32_t c = (uint32_t)quant_code<BITS>(tile[t][i], sf, rsf, zero) & ((1u << CB) - 1u);
+                const uint32_t c = (uint32_t)quant_code<BITS>(tv(t, i), sf, rsf, zero) & ((1u << CB) - 1u);
                 w[(e * CB) / 32] |= c << ((e * CB) % 32);
             }
             *reinterpret_cast<u32x4*>(out + (size_t)k * 16) = w;
@@ -525,10 +543,7 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AppendParams p) {
                 const int i0 = (c % (D / 8)) * 8;
                 u32x4 w;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    w[e] = (__float_as_uint(tile[t][i0 + 2 * e]) >> 16) |
-                           (__float_as_uint(tile[t][i0 + 2 * e + 1]) & 0xffff0000u);
-                }
+                for (int e = 0; e < 4; ++e) w[e] = (uint32_t)tile[t][i0 + 2 * e] | ((uint32_t)tile[t][i0 + 2 * e + 1] << 16);
                 *reinterpret_cast<u32x4*>(stage + t * D + i0) = w;
             }
         }
