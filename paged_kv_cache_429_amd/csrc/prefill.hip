@@ -469,6 +469,9 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
     // by -inf).
     auto commit = [&](int st, uint8_t* buf) {
         uint8_t* vbuf = buf + kStageBlocks * kTile128;
+        // only a stage reaching the context's end has keys to zero (tested
+        // for the whole stage first, so the other stages take no selects)
+        const bool ends = (st + 1) * kStageKeys > ctx;
 #pragma unroll
         for (int j = 0; j < VCH; ++j) {
             const int c = tid + kTileThreads * j;
@@ -477,7 +480,7 @@ void prefill_tile_kernel(PrefillParams p, int ntile) {
             const int sh = c & 1;
             u32x4 v = vstg[j];
             const int key0 = (st * kStageBlocks + blk) * kBlock + 8 * sh;
-            if (key0 + 8 > ctx) {
+            if (ends && key0 + 8 > ctx) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const uint32_t lo = key0 + 2 * e < ctx ? 0x0000ffffu : 0u;
