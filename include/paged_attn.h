@@ -338,8 +338,14 @@ int kv_quantize(const void* src, void* codes, uint16_t* scales,
  * "PagedAttention...": a table maps logical positions to physical slots).
  * k_src, v_src  [num_tokens][n_kv_heads][d_head] of dtype (either may be NULL)
  * slot_mapping  int64 [num_tokens]: slot = block * 16 + offset; a negative
- *               slot skips the token; slots >= num_blocks*16 are skipped
+ *               slot skips the token; slots >= num_blocks*16 are skipped.
+ *               Slots should be distinct: where two tokens name one slot,
+ *               which of them the slot ends up holding is unspecified.
  * k_pool, v_pool  pools with kv_bits = 32 (PA_F32) or 16 (PA_BF16), written
+ *               only at the listed slots (other slots keep their bytes)
+ * Speed: a block whose 16 slots are listed in order by 16 consecutive tokens
+ * is written as whole K and V tiles; any other token costs one scattered
+ * store per V element.
  * ------------------------------------------------------------------------ */
 int paged_kv_write(const void* k_src, const void* v_src, const int64_t* slot_mapping, int num_tokens,
                    void* k_pool, void* v_pool, int num_blocks, int block_size,
