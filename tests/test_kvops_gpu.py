@@ -163,6 +163,44 @@ def test_quantize_ties_bitexact(lib, bits, kind):
     assert np.array_equal(unpack_pool(_img(codes), kind, bits, d), ref_codes)
 
 
+def _fp8_tie_tiles(d, n_kv=2, seed=407):
+    """bf16 slot-form tiles whose quotients x / s land on e4m3 rounding
+    boundaries and one bf16 step either side: each tile's largest magnitude
+    is 56, so its fp16 scale is exactly 56 / 448 = 1/8; the boundaries are the
+    midpoints (1 + (2j+1)/16) 2^e between normal codes and (k + 1/2) / 512
+    between subnormal ones."""
+    g = np.random.default_rng(seed)
+    mids = [(1 + (2 * j + 1) / 16) * 2.0 ** e for e in range(-6, 8) for j in range(8)]
+    mids += [(k + 0.5) / 512 for k in range(8)]
+    mids = np.array([m for m in mids if m < 448], dtype=np.float64) / 8.0
+    nb = 6
+    x = np.zeros((nb * 16, n_kv, d), dtype=np.float32)
+    for b in range(nb):
+        for h in range(n_kv):
+            vals = (g.choice(mids, size=16 * d) * g.choice([-1.0, 1.0], size=16 * d)).astype(np.float32)
+            step = b % 3  # 0: on the boundary; 1: one bf16 step out; 2: one step in
+            bits16 = (vals.view(np.uint32) >> 16).astype(np.int64) + (0 if step == 0 else (1 if step == 1 else -1))
+            vals = (bits16.astype(np.uint32) << 16).view(np.float32)
+            vals[0] = 56.0 * (1 if b % 2 else -1)  # the tile's largest magnitude
+            x[b * 16:(b + 1) * 16, h, :] = vals.reshape(16, d)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("kind", ["k", "v"])
+def test_quantize_fp8_boundaries_bitexact(lib, kind):
+    """e4m3 codes of quotients on rounding boundaries (ties to even) and one
+    bf16 step either side match the oracle's, subnormal range included."""
+    d = 128
+    slots = _fp8_tie_tiles(d)
+    src = np_to_dev(np.ascontiguousarray(pack_pool(slots, kind, 16).view(np.uint16)), "bf16")
+    codes, scales = B.quantize(src, bits=B.PA_KV_FP8, kind=0 if kind == "k" else 1, n_kv_heads=2, d_head=d)
+    torch.cuda.synchronize()
+    ref_codes, ref_scales = oracle.quantize_tiles_fp8(bf16_bits_to_f32(slots))
+    assert (ref_scales.astype(np.float32) == 0.125).all()
+    assert np.array_equal(scales.cpu().numpy().view(np.uint16), ref_scales.view(np.uint16))
+    assert np.array_equal(unpack_pool(_img(codes), kind, 8, d), ref_codes.view(np.int8))
+
+
 def test_quantize_block_subset_and_special_tiles(lib):
     c = make_decode_case(4, 2, 64, "bf16", [64], 403, pool_factor=3.0)
     # tile of zeros and a tile whose fp16 scale overflows
