@@ -14,10 +14,11 @@
 // Slot writes ("KV cache, continuous batching and paged attention", section
 // "The KV cache": each step computes K/V only for the new token and caches
 // them) follow the pool layout: K tiles in 16-byte chunks of consecutive dims
-// (slot-minor), V tiles transposed (dim-major).
-#include "pa_device.h"
-
+// (slot-minor), V tiles transposed (dim-major; int4 in runs of 8 slots of one
+// dim, see v_elem).
 #include <type_traits>
+
+#include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
