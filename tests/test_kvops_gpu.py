@@ -237,14 +237,16 @@ def _quant_case(c, bits):
 
 
 @pytest.mark.parametrize("bits", [8, 4])
-def test_quantized_decode_parity(lib, bits):
-    c = make_decode_case(64, 8, 128, "bf16", [8000, 1, 17, 4000, 515, 8000, 2222, 33], 404, pool_factor=1.1)
+@pytest.mark.parametrize("n_heads,n_kv,d", [(64, 8, 128), (32, 8, 64), (16, 4, 64)])
+def test_quantized_decode_parity(lib, bits, n_heads, n_kv, d):
+    c = make_decode_case(n_heads, n_kv, d, "bf16", [8000, 1, 17, 4000, 515, 8000, 2222, 33], 404 + d + n_heads,
+                         pool_factor=1.1)
     kc, vc, ks, vs = _quant_case(c, bits)
     rk, rks = oracle.quantize_tiles(bf16_bits_to_f32(c.k_slots), bits)
     rv, rvs = oracle.quantize_tiles(bf16_bits_to_f32(c.v_slots), bits)
     # the decode consumes exactly the oracle's codes
-    assert np.array_equal(unpack_pool(_img(kc), "k", bits, 128), rk)
-    assert np.array_equal(unpack_pool(_img(vc), "v", bits, 128), rv)
+    assert np.array_equal(unpack_pool(_img(kc), "k", bits, d), rk)
+    assert np.array_equal(unpack_pool(_img(vc), "v", bits, d), rv)
     got = dev_to_f64(gpu_decode(c, kp=kc, vp=vc, kv_bits=bits, k_scales=ks, v_scales=vs))
     ref = oracle_decode(c, k_slots=oracle.dequantize(rk, rks), v_slots=oracle.dequantize(rv, rvs))
     assert_close(got, ref, "bf16", f"int{bits}")
@@ -308,6 +310,9 @@ def test_quantized_retrieval_probe_exact(lib, bits, d):
         v[:, :, 2] = np.arange(c.n_kv)[None, :]
         for j in range(4):
             v[:, :, 3 + j] = ((blk // 8 ** j) % 8)[:, None]
+    # digits in the last dim blocks too, so every dim block of a V tile is read back
+    v[:, :, d - 1] = ((np.arange(v.shape[0]) % 16) % 8)[:, None]
+    v[:, :, d - 17] = np.arange(c.n_kv)[None, :]
     kcode = np.zeros(c.k_slots.shape, dtype=np.int8)
     kq = oracle.as_f64(c.k_slots, "bf16")
     kcode[kq != 0] = qmax
