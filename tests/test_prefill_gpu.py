@@ -63,11 +63,12 @@ def test_prefill_causal_probe_exact(lib, dtype):
 
 
 @pytest.mark.parametrize("bits", [8, 4, 264])  # 264: fp8 (e4m3)
-def test_prefill_quantized(lib, bits):
-    c = make_prefill_case(32, 8, 128, "bf16", [700, 90], [300, 90], 502 + bits)
+@pytest.mark.parametrize("n_heads,n_kv,d", [(32, 8, 128), (16, 4, 64)])
+def test_prefill_quantized(lib, bits, n_heads, n_kv, d):
+    c = make_prefill_case(n_heads, n_kv, d, "bf16", [700, 90], [300, 90], 502 + bits + d)
     kp, vp = upload_pools(c)
-    kc, ks = B.quantize(kp, bits=bits, kind=0, n_kv_heads=8, d_head=128)
-    vc, vs = B.quantize(vp, bits=bits, kind=1, n_kv_heads=8, d_head=128)
+    kc, ks = B.quantize(kp, bits=bits, kind=0, n_kv_heads=n_kv, d_head=d)
+    vc, vs = B.quantize(vp, bits=bits, kind=1, n_kv_heads=n_kv, d_head=d)
     got = dev_to_f64(gpu_prefill(c, kp=kc, vp=vc, kv_bits=bits, k_scales=ks, v_scales=vs))
     ref = oracle_prefill(c, k=_dequantized(c.k_slots, bits), v=_dequantized(c.v_slots, bits))
     assert_close(got, ref, "bf16", f"prefill kv_bits {bits}")
