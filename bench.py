@@ -144,11 +144,14 @@ def storage_bits(kv_bits):
     return 8 if kv_bits == PA_KV_FP8 else kv_bits
 
 
-def read_ceiling(torch, B, gib=4, reps=10):
+def read_ceiling(torch, B, gib=4, reps=10, decode_bytes=0):
     """The device's measured read bandwidth on the decode's access pattern:
     the library's read probe over a `gib` GiB buffer, once as 4 KiB tiles in
     a random order (one (block, KV head) bf16 tile at d_head 128) and once as
-    a stream; GB/s from HIP events around `reps` passes after two warm-ups."""
+    a stream; GB/s from HIP events around `reps` passes after two warm-ups.
+    With decode_bytes, also random tiles over a buffer of the decode step's
+    own byte count at a few grid sizes (a small grid leaves CUs idle at the
+    end of a pass, as a decode launch of that many workgroups does)."""
     tile = 4096
     n = (gib << 30) // tile
     buf = torch.empty(n * tile, dtype=torch.uint8, device="cuda")
@@ -170,6 +173,26 @@ def read_ceiling(torch, B, gib=4, reps=10):
         out[name] = round(n * tile * reps / (s.elapsed_time(e) * 1e-3) / 1e9, 1)
     del buf, order
     out.update({"buffer_bytes": n * tile, "reps": reps, "loads": "16-byte nontemporal", "workgroups": grid})
+    if decode_bytes:
+        n = max(1, int(decode_bytes) // tile)
+        buf = torch.empty(n * tile, dtype=torch.uint8, device="cuda")
+        buf.fill_(1)
+        order = torch.randperm(n, generator=g).to(torch.int32).cuda()
+        by_grid = {}
+        for grid in (768, 1536, 16384):
+            xo = torch.empty(grid, dtype=torch.int32, device="cuda")
+            for _ in range(2):
+                B.hbm_read_probe(buf, tile, order=order, grid=grid, xor_out=xo)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(2 * reps):
+                B.hbm_read_probe(buf, tile, order=order, grid=grid, xor_out=xo)
+            e.record()
+            torch.cuda.synchronize()
+            by_grid[str(grid)] = round(n * tile * 2 * reps / (s.elapsed_time(e) * 1e-3) / 1e9, 1)
+        del buf, order
+        out["decode_bytes_random_4k_tiles_GBps_by_workgroups"] = by_grid
+        out["decode_bytes_buffer"] = n * tile
     return out
 
 
@@ -620,7 +643,7 @@ def main():
         res["other_bf16_decode"] = extra_decode_configs(torch, B, a.steps, a.warmup, a.layers)
     if not a.no_read_probe:
         # the same box's measured read ceiling, beside the spec peak
-        rc = read_ceiling(torch, B)
+        rc = read_ceiling(torch, B, decode_bytes=byts)
         res["measured_read"] = rc
         res["roofline"]["frac_of_measured_random_tiles"] = round(achieved / rc["random_4k_tiles_GBps"], 4)
     if not a.no_cpu_baseline:
