@@ -115,3 +115,19 @@ def test_workload_pools_match_formula():
     assert [F.paged_waste_slots(n) for n in c.context_lens] == [11, 15, 15, 8]
     assert c.k_slots.nbytes == c.num_blocks * 16 * F.kv_bytes_per_token(1, 2, 64, 4) / 2
     assert int((c.block_tables >= 0).sum()) == sum(F.blocks_needed(n) for n in c.context_lens) == 9
+
+
+@pytest.mark.parametrize("bits,n_tokens,n_kv,d", [(8, 8000, 8, 128), (4, 8000, 8, 128), (8, 17, 2, 64), (4, 1, 4, 64)])
+def test_cache_bytes_counted_from_the_stored_arrays(bits, n_tokens, n_kv, d):
+    """paged_cache_bytes against a count of what a quantized cache stores for
+    one sequence of one layer: the code tiles of its whole blocks, built with
+    the tests' own statement of the pool layout, and one fp16 scale per
+    (block, KV head), for K and for V."""
+    from tests.layout_ref import pack_pool
+    nb = -(-n_tokens // 16)
+    codes = np.zeros((nb * 16, n_kv, d), dtype=np.int8)
+    stored = 0
+    for kind in ("k", "v"):
+        stored += pack_pool(codes, kind, bits).nbytes
+        stored += np.zeros((nb, n_kv), dtype=np.float16).nbytes
+    assert F.paged_cache_bytes(1, n_kv, d, n_tokens, bits) == stored
